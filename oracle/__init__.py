@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for the attention forward pass -- test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package. The product path never does.
+"""
+from .attention import (attention_ref, block_summary, decode_ref, merge_lse,
+                        merge_summaries, split_decode_ref, stream_attention)
+
+__all__ = ["attention_ref", "stream_attention", "block_summary", "merge_summaries",
+           "merge_lse", "decode_ref", "split_decode_ref"]

@@ -1,0 +1,353 @@
+"""Pins for the fp64 oracle against facts fixed outside it: the pages' worked
+examples, closed forms, a pure-Python brute force, scipy's softmax and
+logsumexp, and invariants of softmax attention. CPU only."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+from oracle import (attention_ref, block_summary, decode_ref, merge_lse, merge_summaries,
+                    split_decode_ref, stream_attention)
+from tests.conftest import golden
+
+
+def _close(x, spec):
+    return abs(x - spec["value"]) <= spec["tol"]
+
+
+def _row_problem(scores, values):
+    """One query row whose scores (scale 1) are exactly ``scores``: q = e0, k_j = s_j e0."""
+    n = len(scores)
+    values = np.asarray(values, dtype=np.float64).reshape(n, -1)
+    q = np.zeros((1, 1, 1, 2))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, n, 2))
+    k[0, 0, :, 0] = scores
+    return q, k, values[None, None]
+
+
+# ------------------------------------------------------------ page examples --
+
+def test_t1_four_scores_direct():
+    g = golden("t1_four_scores.json")
+    q, k, v = _row_problem(g["scores"], g["values"])
+    O, L = attention_ref(q, k, v, scale=1.0)
+    assert _close(O[0, 0, 0, 0], g["final"]["output"])
+    assert _close(L[0, 0, 0], g["lse_derived"])
+    assert _close(math.exp(L[0, 0, 0]), g["exp_sum_no_shift"])
+    # with V = I the output row is the probability row itself
+    P, _ = attention_ref(q, k, np.eye(4)[None, None], scale=1.0)
+    for p, want in zip(P[0, 0, 0], g["probabilities"]["value"]):
+        assert abs(p - want) <= g["probabilities"]["tol"]
+    # l relative to the global max 3 is exp(LSE - 3)
+    assert _close(math.exp(L[0, 0, 0] - 3.0), g["final"]["l"])
+
+
+def test_t1_four_scores_streaming_states():
+    g = golden("t1_four_scores.json")
+    q, k, v = _row_problem(g["scores"], g["values"])
+    states = []
+    O, L = stream_attention(q, k, v, 1.0, causal=False, Br=1, Bc=g["tile"],
+                            trace=lambda b, h, i, j, m, l, a, al: states.append((m[0], l[0], a[0, 0], al[0])))
+    assert len(states) == 2
+    m, l, a, _ = states[0]
+    assert m == g["after_tile_A"]["m"]
+    assert _close(l, g["after_tile_A"]["l"]) and _close(a, g["after_tile_A"]["o_unnormalised"])
+    m, l, a, alpha = states[1]
+    assert m == g["final"]["m"]
+    assert _close(alpha, g["correction_factor"])
+    assert _close(l, g["final"]["l"]) and _close(a, g["final"]["o_unnormalised"])
+    assert _close(O[0, 0, 0, 0], g["final"]["output"])
+    assert _close(L[0, 0, 0], g["lse_derived"])
+
+
+def test_t2_block_merge():
+    g = golden("t2_block_merge.json")
+    (m1, l1), (m2, l2) = (block_summary(b) for b in g["blocks"])
+    assert m1 == g["summary_1"]["m"] and _close(l1, g["summary_1"]["l"])
+    assert m2 == g["summary_2"]["m"] and _close(l2, g["summary_2"]["l"])
+    m, l = merge_summaries(m1, l1, m2, l2)
+    assert m == g["merged"]["m"] and _close(l, g["merged"]["l"])
+    assert _close(math.exp(m2 - m) * l2, g["shrink_factor_block_2"])
+    md, ld = block_summary(sum(g["blocks"], []))
+    assert md == m and abs(ld - l) < 1e-14
+
+
+def test_t3_two_tile_trace():
+    g = golden("t3_two_tile_trace.json")
+    q, k, v = _row_problem(g["scores"], g["values"])
+    O, L = attention_ref(q, k, v, scale=1.0)
+    for o, want in zip(O[0, 0, 0], g["output"]["value"]):
+        assert abs(o - want) <= g["output"]["tol"]
+    assert _close(L[0, 0, 0], g["lse_derived"])
+    W, _ = attention_ref(q, k, np.eye(4)[None, None], scale=1.0)
+    for w, want in zip(W[0, 0, 0], g["weights"]["value"]):
+        assert abs(w - want) <= g["weights"]["tol"]
+    states = []
+    O2, _ = stream_attention(q, k, v, 1.0, causal=False, Br=1, Bc=g["tile"],
+                             trace=lambda b, h, i, j, m, l, a, al: states.append((m[0], l[0], a[0].copy(), al[0])))
+    (m1, l1, a1, _), (m2, l2, a2, al2) = states
+    assert m1 == g["tile_1"]["m"] and _close(l1, g["tile_1"]["l"])
+    assert all(abs(x - w) <= g["tile_1"]["a"]["tol"] for x, w in zip(a1, g["tile_1"]["a"]["value"]))
+    assert m2 == g["tile_2"]["m"] and _close(al2, g["tile_2"]["alpha"]) and _close(l2, g["tile_2"]["l"])
+    assert all(abs(x - w) <= g["tile_2"]["a"]["tol"] for x, w in zip(a2, g["tile_2"]["a"]["value"]))
+    assert np.allclose(O2, O, rtol=0, atol=1e-14)
+
+
+def test_t4_causal_tile_behaviour_in_streaming_reference():
+    """Query tile 5 (1-based) at Br=128, Bc=64: loads tiles 1..10, and tile 10
+    leaves rows 513..576 untouched; dropping the mask changes the answer."""
+    g = golden("t4_causal_tiles.json")
+    Br, Bc = g["Br"], g["Bc"]
+    n = g["rows"][1]                      # rows up to 640 reproduce tile 5's geometry
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((1, 1, n, 4)) for _ in range(3))
+    seen = {}
+
+    def tr(b, h, i, j, m, l, a, al):
+        if i == g["query_tile"] - 1:
+            seen[j] = (l.copy(), al.copy())
+    O, L = stream_attention(q, k, v, 0.5, causal=True, Br=Br, Bc=Bc, trace=tr)
+    assert sorted(seen) == list(range(g["loaded_tiles"][0] - 1, g["loaded_tiles"][1]))
+    lo, hi = g["tile_10_silent_rows"][0] - 1 - (g["query_tile"] - 1) * Br, g["tile_10_silent_rows"][1] - (g["query_tile"] - 1) * Br
+    l9, _ = seen[8]
+    l10, al10 = seen[9]
+    assert np.array_equal(l10[lo:hi], l9[lo:hi]) and np.all(al10[lo:hi] == 1.0)
+    Oref, Lref = attention_ref(q, k, v, 0.5, causal=True)
+    assert np.abs(O - Oref).max() < 1e-12 and np.abs(L - Lref).max() < 1e-12
+    Onm, _ = stream_attention(q, k, v, 0.5, causal=True, Br=Br, Bc=Bc, apply_mask=False)
+    rows = slice((g["query_tile"] - 1) * Br, n)
+    assert np.abs(Onm[0, 0, rows] - Oref[0, 0, rows]).max() > 1e-2
+
+
+# -------------------------------------------------------------- brute force --
+
+def _brute(q, k, v, scale, causal):
+    """Scalar loops with math.exp / math.fsum, no arrays, no max shift beyond
+    what the exponent range needs (inputs are kept small)."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, Nq, v.shape[3]))
+    L = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for r in range(Nq):
+                cols = [c for c in range(Nk) if not (causal and c > r)]
+                s = [scale * math.fsum(float(q[b, h, r, t]) * float(k[b, g, c, t]) for t in range(d)) for c in cols]
+                e = [math.exp(x) for x in s]
+                z = math.fsum(e)
+                L[b, h, r] = math.log(z)
+                for t in range(v.shape[3]):
+                    O[b, h, r, t] = math.fsum(e[i] * float(v[b, g, c, t]) for i, c in enumerate(cols)) / z
+    return O, L
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 3), (1, 2, 1, 5, 3), (2, 4, 2, 7, 4), (1, 3, 3, 6, 2)])
+def test_brute_force_tiny(shape, causal):
+    B, Hq, Hkv, N, d = shape
+    rng = np.random.default_rng(hash((shape, causal)) % 2**32)
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d + 1))
+    O, L = attention_ref(q, k, v, 0.7, causal=causal)
+    Ob, Lb = _brute(q, k, v, 0.7, causal)
+    assert np.abs(O - Ob).max() < 1e-12
+    assert np.abs(L - Lb).max() < 1e-12
+
+
+def test_against_scipy_softmax_and_logsumexp():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 37, 16))
+    k = rng.standard_normal((1, 1, 53, 16))
+    v = rng.standard_normal((1, 1, 53, 16))
+    O, L = attention_ref(q, k, v, 0.25)
+    S = 0.25 * np.einsum("id,jd->ij", q[0, 0], k[0, 0])
+    assert np.abs(L[0, 0] - scipy.special.logsumexp(S, axis=1)).max() < 1e-12
+    assert np.abs(O[0, 0] - scipy.special.softmax(S, axis=1) @ v[0, 0]).max() < 1e-12
+    # causal: each row's logsumexp over its visible prefix
+    q2 = rng.standard_normal((1, 1, 40, 8))
+    k2 = rng.standard_normal((1, 1, 40, 8))
+    v2 = rng.standard_normal((1, 1, 40, 8))
+    O2, L2 = attention_ref(q2, k2, v2, 0.5, causal=True)
+    for r in range(40):
+        s = 0.5 * k2[0, 0, :r + 1] @ q2[0, 0, r]
+        assert abs(L2[0, 0, r] - scipy.special.logsumexp(s)) < 1e-12
+        assert np.abs(O2[0, 0, r] - scipy.special.softmax(s) @ v2[0, 0, :r + 1]).max() < 1e-12
+
+
+# ------------------------------------------------------------- closed forms --
+
+def test_closed_form_causal_first_row():
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((2, 3, 33, 8)) for _ in range(3))
+    O, L = attention_ref(q, k, v, 0.3, causal=True)
+    assert np.abs(O[:, :, 0] - v[:, :, 0]).max() < 1e-14
+    assert np.abs(L[:, :, 0] - 0.3 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])).max() < 1e-13
+
+
+def test_closed_form_zero_query_is_mean():
+    rng = np.random.default_rng(12)
+    q = np.zeros((1, 2, 20, 8))
+    k, v = (rng.standard_normal((1, 2, 20, 8)) for _ in range(2))
+    O, L = attention_ref(q, k, v, 1.0)
+    assert np.abs(O - v.mean(axis=2, keepdims=True)).max() < 1e-14
+    assert np.abs(L - math.log(20)).max() < 1e-14
+    Oc, Lc = attention_ref(q, k, v, 1.0, causal=True)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, 21)[None, None, :, None]
+    assert np.abs(Oc - prefix).max() < 1e-13
+    assert np.abs(Lc - np.log(np.arange(1, 21))[None, None]).max() < 1e-14
+
+
+def test_closed_form_single_key_and_dominant_key():
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((1, 1, 1, 8)) for _ in range(3))
+    O, L = attention_ref(q, k, v, 0.9)
+    assert np.abs(O - v).max() < 1e-15 and abs(L[0, 0, 0] - 0.9 * float(q[0, 0, 0] @ k[0, 0, 0])) < 1e-14
+    # one key 200 above every other score: its value row wins to ~1e-80
+    k = np.zeros((1, 1, 6, 2))
+    k[0, 0, :, 0] = [0, 1, 2, 202, -3, 1]
+    qq = np.array([[[[1.0, 0.0]]]])
+    vv = rng.standard_normal((1, 1, 6, 3))
+    O, L = attention_ref(qq, k, vv, 1.0)
+    assert np.abs(O[0, 0, 0] - vv[0, 0, 3]).max() < 1e-12 and abs(L[0, 0, 0] - 202.0) < 1e-12
+
+
+def test_large_scores_do_not_overflow():
+    q = np.full((1, 1, 3, 1), 100.0)
+    k = np.array([[[[10.0], [9.0], [8.0]]]])
+    v = np.array([[[[1.0], [2.0], [3.0]]]])
+    O, L = attention_ref(q, k, v, 1.0)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    w = np.exp(np.array([0.0, -100.0, -200.0]))
+    assert abs(O[0, 0, 0, 0] - (w @ [1, 2, 3]) / w.sum()) < 1e-12
+    assert abs(L[0, 0, 0] - 1000.0 - math.log(w.sum())) < 1e-9
+
+
+# --------------------------------------------------------------- invariants --
+
+@settings(max_examples=25, deadline=None)
+@given(n=st.integers(1, 40), d=st.sampled_from([1, 3, 8]), causal=st.booleans(),
+       seed=st.integers(0, 2**31 - 1))
+def test_invariants(n, d, causal, seed):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    O, L = attention_ref(q, k, v, 0.8, causal=causal)
+    S = 0.8 * q[0, 0] @ k[0, 0].T
+    for r in range(n):
+        vis = slice(0, r + 1) if causal else slice(0, n)
+        cnt = (r + 1) if causal else n
+        smax = S[r, vis].max()
+        assert smax - 1e-12 <= L[0, 0, r] <= smax + math.log(cnt) + 1e-12
+        lo, hi = v[0, 0, vis].min(axis=0), v[0, 0, vis].max(axis=0)
+        assert np.all(O[0, 0, r] >= lo - 1e-12) and np.all(O[0, 0, r] <= hi + 1e-12)
+    # adding a constant to every value row shifts O by that constant
+    O2, _ = attention_ref(q, k, v + 1.5, 0.8, causal=causal)
+    assert np.abs(O2 - O - 1.5).max() < 1e-12
+
+
+def test_key_permutation_invariance_unmasked():
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((1, 2, 30, 8)) for _ in range(3))
+    perm = rng.permutation(30)
+    O, L = attention_ref(q, k, v, 0.4)
+    O2, L2 = attention_ref(q, k[:, :, perm], v[:, :, perm], 0.4)
+    assert np.abs(O - O2).max() < 1e-13 and np.abs(L - L2).max() < 1e-13
+
+
+def test_gqa_equals_explicitly_replicated_heads():
+    """Query head h reads kv head h // G: same as repeating each kv head G times."""
+    rng = np.random.default_rng(22)
+    G, Hkv = 4, 2
+    q = rng.standard_normal((2, G * Hkv, 17, 8))
+    k, v = (rng.standard_normal((2, Hkv, 17, 8)) for _ in range(2))
+    for causal in (False, True):
+        O, L = attention_ref(q, k, v, 0.5, causal=causal)
+        Or, Lr = attention_ref(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.5, causal=causal)
+        assert np.array_equal(O, Or) and np.array_equal(L, Lr)
+        # and the mapping is not the interleaved one
+        Oi, _ = attention_ref(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), 0.5, causal=causal)
+        assert np.abs(Oi - O).max() > 1e-3
+
+
+def test_row_subset_matches_full():
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((1, 2, 50, 8)) for _ in range(3))
+    O, L = attention_ref(q, k, v, 0.5, causal=True)
+    rows = np.array([0, 7, 31, 49])
+    Os, Ls = attention_ref(q[:, :, rows], k, v, 0.5, causal=True, q_positions=rows)
+    assert np.abs(Os - O[:, :, rows]).max() < 1e-14 and np.abs(Ls - L[:, :, rows]).max() < 1e-14
+
+
+def test_row_blocking_does_not_change_result():
+    rng = np.random.default_rng(24)
+    q, k, v = (rng.standard_normal((1, 1, 70, 8)) for _ in range(3))
+    O, L = attention_ref(q, k, v, 0.5, causal=True)
+    O2, L2 = attention_ref(q, k, v, 0.5, causal=True, row_block=16)
+    assert np.abs(O - O2).max() < 1e-15 and np.abs(L - L2).max() < 1e-15
+
+
+@settings(max_examples=20, deadline=None)
+@given(n=st.integers(1, 70), Br=st.sampled_from([1, 4, 16, 32]), Bc=st.sampled_from([1, 3, 8, 16]),
+       causal=st.booleans(), seed=st.integers(0, 2**31 - 1))
+def test_streaming_recurrence_equals_materialised(n, Br, Bc, causal, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 2, n, 4))
+    k, v = (rng.standard_normal((1, 1, n, 4)) for _ in range(2))
+    k[0, 0, rng.integers(0, n)] *= 8.0
+    O, L = stream_attention(q, k, v, 0.6, causal=causal, Br=Br, Bc=Bc)
+    Or, Lr = attention_ref(q, k, v, 0.6, causal=causal)
+    assert np.abs(O - Or).max() < 1e-12 and np.abs(L - Lr).max() < 1e-12
+
+
+# ---------------------------------------------------------- merge / decode --
+
+@settings(max_examples=20, deadline=None)
+@given(n=st.integers(1, 60), split=st.integers(1, 64), seed=st.integers(0, 2**31 - 1))
+def test_split_merge_identity(n, split, seed):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, d, Lmax = 2, 4, 2, 4, 64
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, Hkv, Lmax, d))
+    vc = rng.standard_normal((B, Hkv, Lmax, d))
+    lens = np.array([n, max(1, n // 2)])
+    O, L = decode_ref(q, kc, vc, lens, 0.5)
+    O2, L2 = split_decode_ref(q, kc, vc, lens, 0.5, split)
+    assert np.abs(O - O2).max() < 1e-12 and np.abs(L - L2).max() < 1e-12
+
+
+def test_decode_ignores_padding_and_matches_prefill_row():
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, d, Lmax = 3, 4, 2, 8, 40
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, Hkv, Lmax, d))
+    vc = rng.standard_normal((B, Hkv, Lmax, d))
+    lens = np.array([40, 1, 17])
+    for b in range(B):
+        kc[b, :, lens[b]:] = np.nan
+        vc[b, :, lens[b]:] = np.nan
+    O, L = decode_ref(q, kc, vc, lens, 0.35)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    for b in range(B):
+        n = lens[b]
+        Op, Lp = attention_ref(q[b][None, :, None], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.35)
+        assert np.abs(Op[0, :, 0] - O[b]).max() < 1e-15
+    # a length-1 sequence returns its only value row
+    assert np.abs(O[1] - np.repeat(vc[1, :, 0], Hq // Hkv, axis=0)).max() < 1e-15
+
+
+def test_merge_lse_edge_cases():
+    rng = np.random.default_rng(41)
+    o = rng.standard_normal((3, 4))
+    lse = rng.standard_normal(3)
+    o1, l1 = merge_lse([(o, lse)])
+    assert np.abs(o1 - o).max() < 1e-15 and np.abs(l1 - lse).max() < 1e-15
+    o2, l2 = merge_lse([(o, lse), (np.zeros((3, 4)), np.full(3, -np.inf))])
+    assert np.abs(o2 - o).max() < 1e-15 and np.abs(l2 - lse).max() < 1e-15
+    o3, l3 = merge_lse([(o, lse), (o, lse)])
+    assert np.abs(o3 - o).max() < 1e-15 and np.abs(l3 - lse - math.log(2)).max() < 1e-14
