@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  1. causal GQA prefill, batch 1, 64 query heads over 8 kv heads, N = 8192,
+     d = 128, bf16 (fa_fwd), and
+  2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
+     kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
+     and merge kernel).
+Inputs are generated and uploaded before the timed region. W untimed warmup
+steps, then exactly K timed steps between two device synchronisations. Kernel
+durations come from HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line. ``value`` is the prefill throughput in algorithmic
+TFLOP/s (4*B*Hq*N^2*d, halved for the causal mask); the decode bandwidth in
+algorithmic KV GB/s (every cached K/V byte of every valid token, read once)
+is reported alongside. ``roofline`` / ``roofline_decode`` put both against
+MI355X peaks; ``cpu_baseline`` times the fp64 oracle on a sample of the same
+prefill workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --summarize-trace DIR --out FILE     (rocprofv3 kernel stats -> text)
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE  (HBM traffic per launch)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PREFILL_CFG = "c4a_gqa_8k"
+DECODE_CFG = "c5_decode"
+PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.json")
+KERNEL_SOURCES = ["io_aware_flashattention_amd/csrc/fa_fwd.hip", "io_aware_flashattention_amd/csrc/fa_decode.hip",
+                  "io_aware_flashattention_amd/csrc/fa_device.h"]
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------- the bench --
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import io_aware_flashattention_amd as fa
+    from io_aware_flashattention_amd import cost_model as cm
+    from io_aware_flashattention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    fa.load()
+
+    pc = W.CONFIGS[PREFILL_CFG]
+    dc = W.DECODE_CONFIGS[DECODE_CFG]
+    t0 = time.time()
+    print(f"[bench] generating {pc.name} and {dc.name} inputs", file=sys.stderr, flush=True)
+    qh, kh, vh = W.make_prefill_inputs(pc)
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
+    o = torch.empty_like(q)
+    lse = torch.empty(pc.batch, pc.heads_q, pc.seqlen, dtype=torch.float32, device=dev)
+    dq, dk, dv, lens = W.make_decode_inputs(dc, pad="zero")
+    dq_d, dk_d, dv_d = to_dev(dq), to_dev(dk), to_dev(dv)
+    del dk, dv
+    lens_d = torch.from_numpy(lens).to(dev)
+    do = torch.empty(dc.batch, dc.heads_q, dc.head_dim, dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty(dc.batch, dc.heads_q, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(dc.batch, dc.heads_q, dc.max_len, dc.head_dim), dtype=torch.uint8,
+                     device=dev)
+    # calibration copy of known size (its FETCH/WRITE counters scale the HBM byte counters)
+    csrc = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    del csrc, cdst
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(q, k, v, causal=True, scale=pc.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.decode(dq_d, dk_d, dv_d, lens_d, scale=dc.scale, out=do, lse=dlse, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    print(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms wall", file=sys.stderr, flush=True)
+
+    pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
+    kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    pre_tflops = pre_flops / (pre_avg * 1e-3) / 1e12
+    dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / args.steps
+
+    traffic, traffic_dec = load_traffic()
+    result = {
+        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16, 1% of K rows x8 in the prefill, uniform kv lengths in the decode",
+        "config": {
+            "workload": "causal GQA prefill B1 Hq64 Hkv8 N8192 d128 + split-KV decode B64 Hq64 Hkv8 L~U[1024,32768] d128",
+            "prefill": {"batch": pc.batch, "heads_q": pc.heads_q, "heads_kv": pc.heads_kv, "seq_len": pc.seqlen,
+                        "head_dim": pc.head_dim, "mask": "causal", "flops_per_launch": pre_flops},
+            "decode": {"batch": dc.batch, "heads_q": dc.heads_q, "heads_kv": dc.heads_kv, "head_dim": dc.head_dim,
+                       "sum_kv_len": int(lens.sum()), "kv_bytes_per_launch": kv_bytes,
+                       "split_tokens": 0},
+        },
+        "prefill_ms": round(pre_avg, 4),
+        "decode_ms": round(dec_avg, 4),
+        "decode_value": {"value": round(dec_gbs, 1), "unit": "GB/s", "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fa_fwd (causal, d=128, bf16)"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_dec,
+                            "kernel": "fa_decode (split + merge)"},
+        "kernel_sources": sources_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pc, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else null)."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if d.get("kernel_sources") != sources_hash():
+        return None, None
+    return d.get("prefill_bytes_per_launch"), d.get("decode_bytes_per_launch")
+
+
+def cpu_baseline(pc, seconds: float):
+    """The fp64 oracle, as it stands, on whole query heads of the prefill
+    workload until about ``seconds`` of CPU work; scaled to TFLOP/s with the
+    same algorithmic causal FLOP count as the GPU figure."""
+    import threadpoolctl
+
+    from io_aware_flashattention_amd import cost_model as cm
+    from io_aware_flashattention_amd import workloads as W
+    from oracle import attention_ref
+
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"),
+                  default=1)
+    heads = []
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for h in range(0, pc.heads_q, 9):
+        kvh = h // pc.group
+        q = W.to_f64(W.prefill_slice(pc, "q", 0, h))[None, None]
+        k = W.to_f64(W.prefill_slice(pc, "k", 0, kvh))[None, None]
+        v = W.to_f64(W.prefill_slice(pc, "v", 0, kvh))[None, None]
+        ts = time.perf_counter()
+        attention_ref(q, k, v, pc.scale, causal=True)
+        elapsed += time.perf_counter() - ts
+        heads.append(h)
+        if elapsed >= seconds:
+            break
+    flops = cm.attention_flops(1, len(heads), pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
+    print(f"[bench] cpu baseline: {len(heads)} heads in {elapsed:.1f}s ({time.perf_counter() - t0:.1f}s with input "
+          f"generation)", file=sys.stderr, flush=True)
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle on {len(heads)} whole query heads {heads} of the causal B1 Hq64 Hkv8 N8192 d128 "
+                      f"prefill ({elapsed:.1f} s); host os.cpu_count()={os.cpu_count()}"}
+
+
+# ------------------------------------------------------ profile summaries --
+
+def _read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(d: str, out: str, cmd: str):
+    """rocprofv3 --kernel-trace --stats output directory -> short text table."""
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not stats:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    rows = _read_csv(stats[0])
+    lines = [f"# rocprofv3 kernel statistics", "", f"command: `{cmd}`", "",
+             f"kernel sources: {sources_hash()}", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name", "")
+        short = name if len(name) < 90 else name[:87] + "..."
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        lines.append(f"| `{short}` | {r.get('Calls')} | {avg:.2f} | {float(r.get('MinNs', 0)) / 1e3:.2f} | "
+                     f"{float(r.get('MaxNs', 0)) / 1e3:.2f} | {float(r.get('Percentage', 0)):.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_write: str):
+    """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench -> HBM
+    bytes per launch of each kernel, scaled by what the counters read for the
+    calibration copy of known size."""
+    def per_kernel(dd, counter):
+        files = sorted(glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True))
+        if not files:
+            sys.exit(f"no counter_collection.csv under {dd}")
+        acc = {}
+        for r in _read_csv(files[0]):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r.get("Counter_Value", 0)) * 1024.0)   # KiB -> bytes
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(acc, pred):
+        vals = [v for n, vs in acc.items() if pred(n) for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+    copy_fetch = max((max(vs) for n, vs in fetch.items() if is_copy(n)), default=None)
+    copy_write = max((max(vs) for n, vs in write.items() if is_copy(n)), default=None)
+    sf = COPY_BYTES / copy_fetch if copy_fetch else 1.0
+    sw = COPY_BYTES / copy_write if copy_write else 1.0
+    pre_f = pick(fetch, lambda n: "fwd_kernel" in n)
+    pre_w = pick(write, lambda n: "fwd_kernel" in n)
+    dec_f = (pick(fetch, lambda n: "decode_split" in n) or 0) + (pick(fetch, lambda n: "decode_merge" in n) or 0)
+    dec_w = (pick(write, lambda n: "decode_split" in n) or 0) + (pick(write, lambda n: "decode_merge" in n) or 0)
+    d = {
+        "kernel_sources": sources_hash(),
+        "command_fetch": cmd_fetch, "command_write": cmd_write,
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter_bytes": copy_fetch, "write_counter_bytes": copy_write,
+                             "fetch_scale": sf, "write_scale": sw},
+        "prefill_fetch_bytes": pre_f * sf if pre_f else None, "prefill_write_bytes": pre_w * sw if pre_w else None,
+        "decode_fetch_bytes": dec_f * sf, "decode_write_bytes": dec_w * sw,
+    }
+    d["prefill_bytes_per_launch"] = (d["prefill_fetch_bytes"] or 0) + (d["prefill_write_bytes"] or 0)
+    d["decode_bytes_per_launch"] = d["decode_fetch_bytes"] + d["decode_write_bytes"]
+    with open(out, "w") as f:
+        json.dump(d, f, indent=2)
+    print(json.dumps(d, indent=2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--cmd", nargs="*", default=[], help="commands recorded in a summary")
+    ap.add_argument("--out")
+    args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.out, " ".join(args.cmd))
+    if args.summarize_pmc:
+        cmds = args.cmd + ["", ""]
+        return summarize_pmc(*args.summarize_pmc, args.out, cmds[0], cmds[1])
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU: the attention path here runs on a single MI355X; "
+                 "multi-GPU runs are not part of this build (--gpus 1 only)")
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * fa.h -- C ABI of libfa, an MI355X (gfx950) FlashAttention forward pass.
+ *
+ * Two operations:
+ *
+ *   fa_fwd     exact softmax attention O = softmax(scale * Q K^T + mask) V for
+ *              prefill, computed tile by tile with a running row maximum and
+ *              running row sum so the N x N score and probability matrices never
+ *              reach device memory; it also returns the per-row log-sum-exp.
+ *              (Defined in "How FlashAttention Reduces HBM Traffic Exactly",
+ *              section "The performance problem is data movement, not the
+ *              attention formula"; the loop is the one in "FlashAttention and GPU
+ *              Data Movement", sections 2 and 3.1; the log-sum-exp output is the
+ *              statistic of "FlashAttention Explained: IO-Aware Attention,
+ *              Tiling, Online Softmax and FP8 on Hopper", section "Why the
+ *              statistics are cheap to store".)
+ *
+ *   fa_decode  single-token decode against a KV cache, with the key axis split
+ *              across workgroups; every split writes a partial output and its
+ *              log-sum-exp, and a second small kernel merges the partials
+ *              ("FlashAttention Explained", section "Decoding, Paged and
+ *              Split-KV Variants"; "FlashAttention and GPU Data Movement",
+ *              section 6.1).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates and frees nothing and keeps no state between calls except the
+ *     calling thread's last error message.
+ *   - Calls are asynchronous: FA_OK means the work was enqueued on `stream`
+ *     (a hipStream_t passed as void*, NULL = the default stream). Results are
+ *     valid once the caller synchronises that stream. Device faults surface at
+ *     that synchronisation.
+ *   - Every argument is validated before anything is launched: a non-OK
+ *     status means nothing was enqueued and no output was written.
+ *   - Supported combinations are finite. Anything outside them returns
+ *     FA_ERR_UNSUPPORTED; there is no silent fallback to another algorithm.
+ *   - Strides are in ELEMENTS of the tensor's own dtype. The head dimension is
+ *     always contiguous (stride 1).
+ *   - GQA: query head h reads key/value head h / (heads_q / heads_kv), i.e.
+ *     consecutive query heads share one kv head.
+ *   - The log-sum-exp is natural-log over the scaled, masked scores,
+ *     LSE = m + ln(sum_c exp(s_c - m)), stored as float32.
+ *   - Concurrent calls on different streams are safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, non-finite or non-positive scale */
+  FA_ERR_UNSUPPORTED = 2,        /* valid request outside the implemented set (see each call) */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,/* decode workspace smaller than fa_decode_workspace_bytes() */
+  FA_ERR_HIP = 4                 /* the HIP runtime reported an error at launch */
+} fa_status_t;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype_t;
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 } fa_mask_t;
+
+/*
+ * fa_fwd -- prefill attention forward.
+ *
+ * q   [batch, heads_q,  seqlen_q, head_dim]  in_dtype, strides q_stride  = {b, h, n}
+ * k   [batch, heads_kv, seqlen_k, head_dim]  in_dtype, strides k_stride  = {b, h, n}
+ * v   [batch, heads_kv, seqlen_k, head_dim]  in_dtype, strides v_stride  = {b, h, n}
+ * o   [batch, heads_q,  seqlen_q, head_dim]  out_dtype, strides o_stride = {b, h, n}
+ * lse [batch, heads_q,  seqlen_q] float32, contiguous; may be NULL (not written).
+ *
+ * in_dtype  BF16, or FP32 (values are rounded to bf16, nearest-even, as they are
+ *           staged, and the products run on the bf16 matrix cores).
+ * out_dtype BF16 (O rounded once, nearest-even, from the float32 result) or FP32.
+ * mask      FA_MASK_NONE, or FA_MASK_CAUSAL: key c is visible to query row r iff
+ *           c <= r; requires seqlen_q == seqlen_k. Key tiles wholly in a row
+ *           tile's future are skipped; tiles on the diagonal are masked.
+ * softmax_scale  multiplies Q K^T before the softmax (typically 1/sqrt(head_dim)).
+ *
+ * Supported: head_dim 64 or 128; heads_q % heads_kv == 0; every pointer 16-byte
+ * aligned; every stride a multiple of 8 elements (bf16) or 4 elements (fp32).
+ * Otherwise FA_ERR_UNSUPPORTED. q, k, v must not overlap o or lse.
+ */
+FA_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int32_t batch, int32_t heads_q, int32_t heads_kv,
+                   int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                   const int64_t q_stride[3], const int64_t k_stride[3],
+                   const int64_t v_stride[3], const int64_t o_stride[3],
+                   fa_dtype_t in_dtype, fa_dtype_t out_dtype, fa_mask_t mask,
+                   float softmax_scale, void* stream);
+
+/*
+ * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes
+ * (per-split partial outputs and log-sum-exps, float32). split_tokens <= 0
+ * selects the library default. Returns 0 for invalid sizes.
+ */
+FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
+                                 int32_t head_dim, int32_t split_tokens);
+
+/*
+ * fa_decode -- one query token per sequence against a contiguous KV cache.
+ *
+ * q        [batch, heads_q, head_dim] bf16, contiguous
+ * k_cache  [batch, heads_kv, max_seqlen_k, head_dim] bf16, strides kv_stride = {b, h, n}
+ * v_cache  same shape and strides as k_cache
+ * seqlens_k  DEVICE int32 [batch]: sequence b attends to cache rows
+ *          0 .. seqlens_k[b]-1 and never reads rows at or past that length.
+ *          Values are clamped to [0, max_seqlen_k]; a length of 0 yields O = 0
+ *          and LSE = -inf for that sequence.
+ * o        [batch, heads_q, head_dim] out_dtype, contiguous
+ * lse      [batch, heads_q] float32, contiguous; may be NULL.
+ * split_tokens  keys per split (multiple of 64); <= 0 selects the default.
+ *          LSE does not depend on it beyond float32 rounding; O may move by
+ *          bf16 rounding of the probabilities, which each split takes relative
+ *          to its own running maximum.
+ * workspace      device buffer of at least fa_decode_workspace_bytes(...) bytes,
+ *          16-byte aligned; its contents on entry do not matter and are
+ *          overwritten. Two calls that share a workspace must be ordered.
+ *
+ * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
+ * bf16 q and cache; pointers 16-byte aligned; kv strides multiples of 8.
+ */
+FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens_k, void* o, float* lse,
+                      int32_t batch, int32_t heads_q, int32_t heads_kv,
+                      int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                      fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. Never NULL. */
+FA_API const char* fa_status_string(fa_status_t status);
+
+/* Detail of the calling thread's most recent non-OK return ("" if none). */
+FA_API const char* fa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

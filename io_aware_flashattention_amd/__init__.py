@@ -1,5 +1,9 @@
 """MI355X (gfx950) FlashAttention forward pass: prefill and split-KV decode.
 
 The compute path is the C-ABI library ``libfa.so`` built from ``csrc/``;
-``fwd`` and ``decode`` marshal torch tensors into it.
+``fwd`` and ``decode`` marshal torch tensors into it and raise if it is
+missing or refuses a call.
 """
+from ._lib import FaError, decode, decode_workspace_bytes, fwd, load
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "load", "FaError"]

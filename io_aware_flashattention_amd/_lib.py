@@ -1,0 +1,151 @@
+"""ctypes binding of libfa (include/fa.h) over torch tensors.
+
+Argument marshalling only: every step of attention runs in the HIP kernels of
+libfa.so. torch supplies device memory and the current stream. If the library
+is missing or a call is unsupported, these functions raise; there is no other
+code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
+FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
+                3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
+EXPORTED = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode", "fa_status_string",
+            "fa_last_error_message")
+
+_i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load():
+    """Load libfa.so (built by ``python -m io_aware_flashattention_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(f"{LIB_PATH} is not built; run python -m io_aware_flashattention_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                           _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_float, _vp]
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.fa_decode.restype = ctypes.c_int
+    lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
+                              ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_last_error_message.restype = ctypes.c_char_p
+    lib.fa_last_error_message.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, load().fa_last_error_message().decode())
+
+
+def _strides3(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, N, d] tensor with contiguous last dimension")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if dt == torch.float32:
+        return FA_DTYPE_FP32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: float | None = None, out_dtype: torch.dtype | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+    """Prefill attention. q [B,Hq,N,d], k/v [B,Hkv,Nk,d] on the GPU (bf16 or fp32).
+
+    Returns (O, LSE); LSE is float32 [B,Hq,N] (None if ``lse`` is False).
+    """
+    lib = load()
+    B, Hq, N, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    lse.data_ptr() if lse is not None else None,
+                    B, Hq, Hkv, N, Nk, d, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
+                    _dtype_code(q.dtype), _dtype_code(out.dtype),
+                    FA_MASK_CAUSAL if causal else FA_MASK_NONE, float(scale), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def decode_workspace_bytes(batch: int, heads_q: int, max_seqlen: int, head_dim: int, split_tokens: int = 0) -> int:
+    return int(load().fa_decode_workspace_bytes(batch, heads_q, max_seqlen, head_dim, split_tokens))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
+           scale: float | None = None, split_tokens: int = 0, out_dtype: torch.dtype | None = None,
+           out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+           workspace: torch.Tensor | None = None):
+    """Split-KV decode. q [B,Hq,d] bf16; caches [B,Hkv,Lmax,d] bf16; seqlens int32 [B] on the GPU."""
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+        raise ValueError("seqlens must be a contiguous int32 tensor of length batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = decode_workspace_bytes(B, Hq, Lmax, d, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                       out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                       B, Hq, Hkv, Lmax, d, _strides3(k_cache), _dtype_code(out.dtype), float(scale),
+                       int(split_tokens), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       _stream(q.device))
+    _check(st)
+    return out, lse

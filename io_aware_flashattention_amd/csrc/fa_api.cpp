@@ -1,0 +1,193 @@
+// C ABI of libfa: argument validation, instantiation choice and launch.
+// Every check runs before anything is enqueued, so an error return means no
+// work was launched and no output was touched. Unsupported combinations fail
+// loudly instead of falling back to another algorithm.
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status_t fail(fa_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+fa_status_t ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte span [lo, hi) a strided [batch, heads, rows, head_dim] tensor touches.
+void span(const void* base, const int64_t st[3], int64_t nb, int64_t nh, int64_t nr, int64_t d,
+          int64_t elem, uintptr_t* lo, uintptr_t* hi) {
+  int64_t last = (nb - 1) * st[0] + (nh - 1) * st[1] + (nr - 1) * st[2] + d;
+  *lo = reinterpret_cast<uintptr_t>(base);
+  *hi = *lo + static_cast<uintptr_t>(last * elem);
+}
+
+bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error_message(void) { return g_last_error.c_str(); }
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int32_t batch, int32_t heads_q, int32_t heads_kv,
+                   int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                   const int64_t q_stride[3], const int64_t k_stride[3],
+                   const int64_t v_stride[3], const int64_t o_stride[3],
+                   fa_dtype_t in_dtype, fa_dtype_t out_dtype, fa_mask_t mask,
+                   float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: q, k, v and o must be non-null");
+  if (!q_stride || !k_stride || !v_stride || !o_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: stride arrays must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: sizes must be positive (batch=%d heads_q=%d heads_kv=%d seqlen_q=%d seqlen_k=%d head_dim=%d)",
+                batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: softmax_scale must be finite and positive (got %g)", (double)softmax_scale);
+  if (in_dtype != FA_DTYPE_BF16 && in_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: unknown in_dtype %d", (int)in_dtype);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: unknown out_dtype %d", (int)out_dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: unknown mask %d", (int)mask);
+  for (int i = 0; i < 3; ++i)
+    if (q_stride[i] < 0 || k_stride[i] < 0 || v_stride[i] < 0 || o_stride[i] < 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: strides must be non-negative");
+
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head_dim %d not supported (64 or 128)", head_dim);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+  if (mask == FA_MASK_CAUSAL && seqlen_q != seqlen_k)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: causal mask needs seqlen_q == seqlen_k (got %d, %d)", seqlen_q, seqlen_k);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: q, k, v and o must be 16-byte aligned");
+  const int in_vec = in_dtype == FA_DTYPE_BF16 ? 8 : 4;
+  const int out_vec = out_dtype == FA_DTYPE_BF16 ? 8 : 4;
+  for (int i = 0; i < 3; ++i) {
+    if (q_stride[i] % in_vec || k_stride[i] % in_vec || v_stride[i] % in_vec)
+      return fail(FA_ERR_UNSUPPORTED, "fa_fwd: q/k/v strides must be multiples of %d elements", in_vec);
+    if (o_stride[i] % out_vec)
+      return fail(FA_ERR_UNSUPPORTED, "fa_fwd: o strides must be multiples of %d elements", out_vec);
+  }
+  const int64_t in_b = in_dtype == FA_DTYPE_BF16 ? 2 : 4, out_b = out_dtype == FA_DTYPE_BF16 ? 2 : 4;
+  uintptr_t o0, o1, a0, a1;
+  span(o, o_stride, batch, heads_q, seqlen_q, head_dim, out_b, &o0, &o1);
+  span(q, q_stride, batch, heads_q, seqlen_q, head_dim, in_b, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: o overlaps q");
+  span(k, k_stride, batch, heads_kv, seqlen_k, head_dim, in_b, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: o overlaps k");
+  span(v, v_stride, batch, heads_kv, seqlen_k, head_dim, in_b, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: o overlaps v");
+  const int br = fa::fwd_query_tile_rows();
+  const int64_t n_qtiles = (seqlen_q + br - 1) / br;
+  if ((int64_t)batch * heads_q * n_qtiles > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: problem too large for one launch");
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    p.q_stride[i] = q_stride[i]; p.k_stride[i] = k_stride[i];
+    p.v_stride[i] = v_stride[i]; p.o_stride[i] = o_stride[i];
+  }
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+  p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+  p.n_qtiles = (int)n_qtiles;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = mask == FA_MASK_CAUSAL;
+  p.in_fp32 = in_dtype == FA_DTYPE_FP32;
+  p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  hipError_t e = fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
+                                 int32_t head_dim, int32_t split_tokens) {
+  if (batch <= 0 || heads_q <= 0 || max_seqlen_k <= 0 || head_dim <= 0) return 0;
+  const int split = split_tokens > 0 ? split_tokens : fa::decode_default_split();
+  const int64_t splits = (max_seqlen_k + split - 1) / split;
+  return static_cast<size_t>((int64_t)batch * heads_q * splits * (head_dim + 1) * 4);
+}
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens_k, void* o, float* lse,
+                      int32_t batch, int32_t heads_q, int32_t heads_kv,
+                      int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                      fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !kv_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: q, caches, seqlens_k, o and kv_stride must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || max_seqlen_k <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: sizes must be positive");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: softmax_scale must be finite and positive (got %g)", (double)softmax_scale);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: unknown out_dtype %d", (int)out_dtype);
+  for (int i = 0; i < 3; ++i)
+    if (kv_stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: strides must be non-negative");
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_decode: head_dim %d not supported (128)", head_dim);
+  if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head",
+                heads_q, heads_kv);
+  const int split = split_tokens > 0 ? split_tokens : fa::decode_default_split();
+  if (split % 64 != 0) return fail(FA_ERR_UNSUPPORTED, "fa_decode: split_tokens (%d) must be a multiple of 64", split);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode: q, caches, o and workspace must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (kv_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "fa_decode: kv strides must be multiples of 8 elements");
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, max_seqlen_k, head_dim, split);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  const int64_t splits = (max_seqlen_k + split - 1) / split;
+  if ((int64_t)batch * heads_kv * splits / 4 + 1 > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode: problem too large for one launch");
+
+  fa::DecodeParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.seqlens = seqlens_k; p.o = o; p.lse = lse;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + (int64_t)batch * heads_q * splits * head_dim;
+  for (int i = 0; i < 3; ++i) p.kv_stride[i] = kv_stride[i];
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+  p.max_seqlen = max_seqlen_k; p.head_dim = head_dim;
+  p.split_tokens = split; p.max_splits = (int)splits;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  hipError_t e = fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal interface between the C ABI (fa_api.hip) and the kernel launchers.
+// Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  int batch, heads_q, heads_kv, group, seqlen_q, seqlen_k, head_dim;
+  int n_qtiles;
+  float scale_log2;  // softmax scale * log2(e)
+  bool causal, in_fp32, out_fp32;
+};
+
+struct DecodeParams {
+  const void* q;       // [B, Hq, d] bf16
+  const void* k;       // cache [B, Hkv, Lmax, d] bf16
+  const void* v;
+  const int32_t* seqlens;
+  void* o;             // [B, Hq, d]
+  float* lse;          // [B, Hq] or null
+  float* part_o;       // workspace [B, Hq, max_splits, d]
+  float* part_lse;     // workspace [B, Hq, max_splits]
+  int64_t kv_stride[3];
+  int batch, heads_q, heads_kv, group, max_seqlen, head_dim;
+  int split_tokens, max_splits;
+  float scale_log2;
+  bool out_fp32;
+};
+
+int fwd_query_tile_rows();
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+
+int decode_default_split();
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -225,3 +225,30 @@ def to_f64(x: np.ndarray) -> np.ndarray:
     if x.dtype == np.uint16:
         return bf16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def make_random_prefill(batch: int, heads_q: int, heads_kv: int, seqlen_q: int, seqlen_k: int,
+                        head_dim: int, dtype: str = "bf16", seed: int = 0, heavy_frac: float = 0.0):
+    """Q [B,Hq,Nq,d], K/V [B,Hkv,Nk,d] for arbitrary (ragged, small) test shapes.
+
+    Same recipe as the named workloads: per-slice PCG64 streams, N(0,1)
+    float32 rounded to bf16 (kept as float32 for dtype="fp32"), and an
+    optional fraction of K rows per (b, kv head) multiplied by 8.
+    """
+    conv = (lambda x: x) if dtype == "fp32" else f32_to_bf16_bits
+    q = np.stack([np.stack([conv(_normal_f32(seed, TAG_Q, b, h, (seqlen_q, head_dim))) for h in range(heads_q)])
+                  for b in range(batch)])
+    ks, vs = [], []
+    for b in range(batch):
+        kb, vb = [], []
+        for h in range(heads_kv):
+            kf = _normal_f32(seed, TAG_K, b, h, (seqlen_k, head_dim))
+            n = int(round(heavy_frac * seqlen_k))
+            if n:
+                rng = np.random.Generator(np.random.PCG64([seed, TAG_HEAVY, b, h]))
+                kf[rng.choice(seqlen_k, size=n, replace=False)] *= np.float32(8.0)
+            kb.append(conv(kf))
+            vb.append(conv(_normal_f32(seed, TAG_V, b, h, (seqlen_k, head_dim))))
+        ks.append(np.stack(kb))
+        vs.append(np.stack(vb))
+    return q, np.stack(ks), np.stack(vs)

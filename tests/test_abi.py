@@ -1,0 +1,126 @@
+"""The C-ABI library: loads, exports exactly what include/fa.h declares, and
+rejects bad arguments before touching the GPU. CPU only: every call below
+fails validation, which runs before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from io_aware_flashattention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert decl == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert funcs == decl
+    lib = _lib.load()
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_string(code).decode() == name
+    assert lib.fa_status_string(99).decode() == "FA_ERR_UNKNOWN"
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=None, B=1, Hq=2, Hkv=1,
+             Nq=64, Nk=64, d=128, qs=(16384, 8192, 128), ks=(8192, 8192, 128), vs=(8192, 8192, 128),
+             os_=(16384, 8192, 128), ind=0, outd=0, mask=0, scale=0.125)
+    a.update(kw)
+    arr = lambda t: (ctypes.c_int64 * 3)(*t) if t is not None else None
+    st = lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                    arr(a["qs"]), arr(a["ks"]), arr(a["vs"]), arr(a["os_"]), a["ind"], a["outd"], a["mask"],
+                    a["scale"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(qs=None), 1, "stride"),
+    (dict(B=0), 1, "positive"),
+    (dict(Nk=-3), 1, "positive"),
+    (dict(scale=float("nan")), 1, "softmax_scale"),
+    (dict(scale=0.0), 1, "softmax_scale"),
+    (dict(ind=7), 1, "in_dtype"),
+    (dict(mask=5), 1, "mask"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(Hq=3, Hkv=2), 2, "multiple"),
+    (dict(mask=1, Nq=64, Nk=80), 2, "causal"),
+    (dict(q=FAKE + 8), 2, "aligned"),
+    (dict(qs=(16384, 8192, 132)), 2, "multiples"),
+    (dict(ind=1, qs=(16384, 8192, 130)), 2, "multiples"),
+    (dict(o=FAKE + 0x100), 1, "overlaps"),
+])
+def test_fwd_rejects_before_launch(kw, status, needle):
+    st, msg = _fwd(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+def _dec(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lens=FAKE + 0x300000, o=FAKE + 0x400000, lse=None,
+             B=2, Hq=16, Hkv=2, L=4096, d=128, kvs=(2 * 4096 * 128, 4096 * 128, 128), outd=0, scale=0.0884,
+             split=0, ws=FAKE + 0x800000, wsb=1 << 30)
+    a.update(kw)
+    kvs = (ctypes.c_int64 * 3)(*a["kvs"]) if a["kvs"] is not None else None
+    st = lib.fa_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["L"],
+                       a["d"], kvs, a["outd"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lens=None), 1, "non-null"),
+    (dict(kvs=None), 1, "non-null"),
+    (dict(L=0), 1, "positive"),
+    (dict(scale=float("inf")), 1, "softmax_scale"),
+    (dict(d=64), 2, "head_dim"),
+    (dict(Hq=16, Hkv=3), 2, "multiple"),
+    (dict(Hq=66, Hkv=1), 2, "at most 32"),
+    (dict(split=100), 2, "multiple of 64"),
+    (dict(k=FAKE + 4), 2, "aligned"),
+    (dict(kvs=(2 * 4096 * 128, 4096 * 128, 132)), 2, "multiples"),
+    (dict(wsb=1000), 3, "workspace"),
+    (dict(ws=None), 3, "workspace"),
+])
+def test_decode_rejects_before_launch(kw, status, needle):
+    st, msg = _dec(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_decode_workspace_size():
+    lib = _lib.load()
+    # 64 sequences x 64 heads x ceil(32768 / 1024) splits x (128 + 1) floats
+    assert lib.fa_decode_workspace_bytes(64, 64, 32768, 128, 1024) == 64 * 64 * 32 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 100, 128, 64) == 2 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(0, 1, 100, 128, 64) == 0
+    assert lib.fa_decode_workspace_bytes(2, 8, 1000, 128, 0) > 0
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(FileNotFoundError):
+        _lib.load()
