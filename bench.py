@@ -197,7 +197,7 @@ def cpu_baseline(pc, seconds: float):
     heads = []
     t0 = time.perf_counter()
     elapsed = 0.0
-    for h in range(0, pc.heads_q, 9):
+    for h in [(9 * i) % pc.heads_q for i in range(pc.heads_q)]:   # spread over kv groups
         kvh = h // pc.group
         q = W.to_f64(W.prefill_slice(pc, "q", 0, h))[None, None]
         k = W.to_f64(W.prefill_slice(pc, "k", 0, kvh))[None, None]
