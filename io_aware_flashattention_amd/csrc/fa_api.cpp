@@ -111,8 +111,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: o overlaps k");
   span(v, v_stride, batch, heads_kv, seqlen_k, head_dim, in_b, &a0, &a1);
   if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd: o overlaps v");
-  const int br = fa::fwd_query_tile_rows();
-  const int64_t n_qtiles = (seqlen_q + br - 1) / br;
+  const int64_t n_qtiles = (seqlen_q + 63) / 64;          // bound over every kernel's row tile
   if ((int64_t)batch * heads_q * n_qtiles > 0x7fffffffLL)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd: problem too large for one launch");
 
@@ -124,7 +123,6 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   }
   p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
   p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
-  p.n_qtiles = (int)n_qtiles;
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = mask == FA_MASK_CAUSAL;
   p.in_fp32 = in_dtype == FA_DTYPE_FP32;

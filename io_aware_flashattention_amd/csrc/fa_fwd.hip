@@ -1,58 +1,89 @@
-// Prefill attention forward for gfx950: exact softmax attention computed one
-// 64-key tile at a time with a running row maximum and running row sum, so the
-// N x N scores never leave the chip.
+// Prefill attention forward for bf16 inputs on gfx950: exact softmax attention
+// computed one 64-key tile at a time with a running row maximum and running
+// row sum, so the N x N scores never leave the chip.
 //
 // The loop is the FlashAttention-2 order ("FlashAttention and GPU Data
 // Movement", section 2 and the recurrence of section 3.1): a workgroup owns a
-// 128-row query tile, streams K/V tiles through LDS, keeps an unnormalised
+// tile of query rows, streams K/V tiles through LDS, keeps an unnormalised
 // float32 accumulator in registers, divides once at the end and writes O and
 // the per-row log-sum-exp once. Under the causal mask, tiles wholly in the
 // future are not loaded (the skip bound) and only tiles crossing the diagonal
 // are masked, elementwise, before the row statistics see them (section 2.1).
 //
-// Mapping onto the CDNA4 compute unit (four 64-lane waves per workgroup, two
-// workgroups per CU so one wave's softmax overlaps another's matrix work):
-//   * wave w owns query rows q0+32w .. q0+32w+31; lane l owns row l % 32;
-//   * S^T = K_tile Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, rows on N);
-//     K rows are fed in sigma order so the score accumulator is already the
-//     B operand of O^T += V^T P^T: no register shuffles between the two;
+// Mapping onto the CDNA4 compute unit:
+//   * NW waves per workgroup, wave w owns query rows q0+32w .. q0+32w+31 and
+//     lane l owns row l % 32; two waves share each SIMD so one wave's softmax
+//     overlaps the other's matrix work;
+//   * K/V tiles move global -> LDS by direct DMA loads (no register staging),
+//     STAGES tiles deep, one barrier per tile; rows past the sequence end are
+//     clamped to the last row and masked, so the loads need no branches;
+//   * S^T = K_tile Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, rows on N). K
+//     rows are read in sigma order so the score accumulator is already the B
+//     operand of O^T += V^T P^T; V stays row-major in LDS and its A operand
+//     (eight consecutive keys of one d per lane) comes from transposing
+//     ds_read_b64_tr_b16 reads;
 //   * the softmax runs in base 2 with scale*log2(e) folded into one FMA per
-//     score; a row's keys are split between lane l and lane l^32, joined with
-//     one permlane32 swap for the max and one for the sum;
-//   * K is staged as [key][d], V transposed as [d][key], both with XOR-swizzled
-//     16-byte chunks, double-buffered: the next tile's global loads are in
-//     flight while the current tile is computed.
-// float32 inputs keep the same structure with every operand split into a
-// bf16 high part and a bf16 remainder (x = hi + lo to about 16 significant
-// bits); each product is hi*hi + hi*lo + lo*hi on the same bf16 matrix
-// instructions, so float32 data is not truncated to 8 significant bits.
+//     score; a row's keys are split between lane l and lane l^32 and joined
+//     with one permlane32 swap;
+//   * the accumulator is rescaled only when some row's maximum grows by more
+//     than 2^8 (between rescales exp2 arguments stay <= 8): O / l and
+//     m + log2 l use one consistent base, so the result is unchanged. This is
+//     the conditional rescaling of "FlashAttention Explained: IO-Aware
+//     Attention, Tiling, Online Softmax and FP8 on Hopper" (FlashAttention-4
+//     section). With a stale base the dominant weight is no longer exactly 1,
+//     so two row sums are kept: O is divided by the sum of the bf16-rounded
+//     weights that actually enter P V (an exactly normalised combination of V
+//     rows), and the log-sum-exp uses the float32 sum of the weights.
 #include "fa_device.h"
 #include "fa_launch.h"
+
+#ifndef FA_FWD_NW128
+#define FA_FWD_NW128 8       // waves per workgroup at head_dim 128
+#endif
+#ifndef FA_FWD_STAGES128
+#define FA_FWD_STAGES128 3   // K/V tiles in flight at head_dim 128
+#endif
 
 namespace fa {
 
 namespace {
 
-constexpr int BR = 128;   // query rows per workgroup
-constexpr int BC = 64;    // keys per tile
-constexpr int NT = 256;   // threads per workgroup
+constexpr int BC = 64;       // keys per tile
+constexpr float kRescaleThreshold = 8.f;
 
-template <typename TIn> constexpr int min_blocks() { return sizeof(TIn) == 2 ? 2 : 1; }
+// V tile swizzle for the transposing reads: a 16-lane group reads 4
+// consecutive rows x 32 bytes; XOR-ing the 16-byte chunk index by 2*(row%4)
+// puts the 4 rows on disjoint bank groups.
+__device__ __forceinline__ int vswz_tr(int r) { return 2 * (r & 3); }
 
-template <int D, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(NT, min_blocks<TIn>()) void fwd_kernel(const FwdParams p) {
-  constexpr bool SPLIT = sizeof(TIn) == 4;   // float32 inputs: hi/lo bf16 planes
-  constexpr int NP = SPLIT ? 2 : 1;          // LDS planes per operand
-  constexpr int DCH = D / 8;                 // 16-byte chunks per row
+// LDS pointer type for the direct global -> LDS loads (the host pass of the
+// compiler needs the address space spelled out).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace
+
+namespace detail {
+
+template <int D, bool CAUSAL, typename TOut, int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdParams p) {
+  constexpr int BRW = 32 * NW;               // query rows per workgroup
   constexpr int KSTEPS = D / 16;             // k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
-  constexpr int K_LOADS = BC * DCH / NT;     // K chunks per thread
-  constexpr int V_ITEMS = (BC / 4) * DCH;    // (4 keys x 8 d) items per V tile
-  constexpr int TILE = BC * D;               // elements per K or Vt tile
-  using IO = In<TIn>;
-  static_assert(K_LOADS >= 1 && BC * DCH % NT == 0, "tile / thread mismatch");
+  constexpr int TILE = BC * D;               // bf16 elements per K or V tile
+  constexpr int ROWB = 2 * D;                // bytes per K/V row
+  constexpr int NLD = TILE * 2 / 1024;       // 1-KB DMA writes per operand tile
+  constexpr int LPW = NLD / NW;              // of those, per wave
+  static_assert(NLD % NW == 0, "tile / wave mismatch");
+  static_assert(STAGES >= 2, "");
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * NP * TILE];   // [stage][K planes | Vt planes]
+  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE];   // [stage][K, V][TILE]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -60,7 +91,8 @@ __global__ __launch_bounds__(NT, min_blocks<TIn>()) void fwd_kernel(const FwdPar
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
-  // ---- which (batch, head, query tile): XCD-aware, heavy causal tiles first
+  // ---- which (batch, head, query tile): XCD-aware, heavy causal tiles first,
+  // the query heads of one kv head next to each other
   const int n = gridDim.x;
   const int wg = blockIdx.x;
   const int xcd = wg & 7, slot = wg >> 3;
@@ -75,221 +107,195 @@ __global__ __launch_bounds__(NT, min_blocks<TIn>()) void fwd_kernel(const FwdPar
   const int hq = kvh * p.group + g;
   const int qt = CAUSAL ? p.n_qtiles - 1 - t : t;
 
-  const TIn* __restrict__ qp = reinterpret_cast<const TIn*>(p.q) + b * p.q_stride[0] + hq * p.q_stride[1];
-  const TIn* __restrict__ kp = reinterpret_cast<const TIn*>(p.k) + b * p.k_stride[0] + kvh * p.k_stride[1];
-  const TIn* __restrict__ vp = reinterpret_cast<const TIn*>(p.v) + b * p.v_stride[0] + kvh * p.v_stride[1];
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_stride[0] + hq * p.q_stride[1];
+  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + b * p.k_stride[0] + kvh * p.k_stride[1];
+  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_stride[0] + kvh * p.v_stride[1];
+  const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
 
-  const int q0 = qt * BR;
+  const int q0 = qt * BRW;
   const int wrow0 = q0 + wave * 32;
   const int row = wrow0 + r32;
   const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;    // skip bound
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  // ---- DMA plan: this lane's 16-byte chunk of each 1-KB write
+  int dma_row[LPW], dma_k[LPW], dma_v[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (wave * LPW + i) * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    dma_row[i] = r;
+    dma_k[i] = 8 * (pc ^ kswz(r));
+    dma_v[i] = 8 * (pc ^ vswz_tr(r));
+  }
+  auto issue = [&](int tile, int ST) {
+    const int kv0 = tile * BC;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int key = min(kv0 + dma_row[i], nk - 1);
+      __bf16* dk = smem + ST * 2 * TILE + (wave * LPW + i) * 512;
+      __builtin_amdgcn_global_load_lds((const void*)(kp + key * ks2 + dma_k[i]), (lds_void*)dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + key * vs2 + dma_v[i]), (lds_void*)(dk + TILE), 16, 0, 0);
+    }
+  };
 
   // ---- this lane's query row as B-operand fragments (rows past the end are 0)
-  bf16x8 qf[KSTEPS], ql[SPLIT ? KSTEPS : 1];
+  bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int kc = 0; kc < KSTEPS; ++kc) {
-    auto raw = row < nq ? IO::load(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half) : IO::zero();
-    if constexpr (SPLIT) {
-      split_hi_lo(raw, qf[kc], ql[kc]);
-    } else {
-      qf[kc] = as_bf16x8(IO::pack(raw));
+  for (int kc = 0; kc < KSTEPS; ++kc)
+    qf[kc] = as_bf16x8(row < nq ? load16(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half)
+                                : u32x4{0, 0, 0, 0});
+
+  // ---- lane-constant LDS offsets (elements) of the fragment reads
+  int koff[KSTEPS];
+  {
+    const int r = sigma32(r32);
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz(r));
+  }
+  int voff[DBLK];
+  {
+    const int gg = lane >> 4, i = lane & 15;
+    const int r = 8 * (gg >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
+      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_tr(r)) + (col & 7);
     }
   }
 
-  const int kv_end = CAUSAL ? min(nk, q0 + BR) : nk;   // skip bound
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  // ---- global -> register staging of one K/V tile
-  typename IO::Raw kreg[K_LOADS];
-  typename IO::Raw vreg[4];
-  const int v_item = tid;                       // one (4-key x 8-d) item per thread
-  const int v_dc = v_item % DCH, v_kg = v_item / DCH;
-  const bool v_on = V_ITEMS >= NT || v_item < V_ITEMS;
-
-  auto load_tile = [&](int j) {
-    const int kv0 = j * BC;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + NT * i;
-      const int key = c / DCH, ch = c % DCH;
-      kreg[i] = (kv0 + key < nk) ? IO::load(kp + (int64_t)(kv0 + key) * p.k_stride[2] + 8 * ch) : IO::zero();
-    }
-    if (v_on) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kv0 + 4 * v_kg + i;
-        vreg[i] = (key < nk) ? IO::load(vp + (int64_t)key * p.v_stride[2] + 8 * v_dc) : IO::zero();
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    __bf16* ks = smem + stage * 2 * NP * TILE;     // K planes: hi [, lo]
-    __bf16* vs = ks + NP * TILE;                   // Vt planes: hi [, lo]
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + NT * i;
-      const int key = c / DCH, ch = c % DCH;
-      const int at = key * D + 8 * (ch ^ kswz(key));
-      if constexpr (SPLIT) {
-        bf16x8 hi, lo;
-        split_hi_lo(kreg[i], hi, lo);
-        *reinterpret_cast<bf16x8*>(ks + at) = hi;
-        *reinterpret_cast<bf16x8*>(ks + TILE + at) = lo;
-      } else {
-        *reinterpret_cast<u32x4*>(ks + at) = IO::pack(kreg[i]);
-      }
-    }
-    if (v_on) {
-#pragma unroll
-      for (int pl = 0; pl < NP; ++pl) {
-        u32x4 w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (SPLIT) {
-            bf16x8 hi, lo;
-            split_hi_lo(vreg[i], hi, lo);
-            w[i] = __builtin_bit_cast(u32x4, pl == 0 ? hi : lo);
-          } else {
-            w[i] = IO::pack(vreg[i]);
-          }
-        }
-        // element e of keys 4kg..4kg+3 -> Vt[8*dc + e][4kg .. 4kg+3]
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu, a1 = (w[1][e >> 1] >> sh) & 0xffffu;
-          const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu, a3 = (w[3][e >> 1] >> sh) & 0xffffu;
-          const int d = 8 * v_dc + e;
-          const int chunk = (v_kg >> 1) ^ vswz(d);
-          *reinterpret_cast<u32x2*>(vs + pl * TILE + d * BC + 8 * chunk + 4 * (v_kg & 1)) =
-              u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
-        }
-      }
-    }
-  };
-
   // ---- running state of this lane's row
-  const float c2 = p.scale_log2;           // scale * log2(e): scores in base-2 units
-  float m_run = kNegInf;                   // running max (base-2 units)
-  float l_run = 0.f;                       // running sum of exp2(s - m_run)
+  const float c2 = p.scale_log2;
+  float m_run = kNegInf;          // base of the exponentials (base-2 units)
+  float l_run = 0.f;              // float32 sum of the weights (for the log-sum-exp)
+  float l_o = 0.f;                // sum of the bf16-rounded weights (normalises O)
   f32x16 o[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  auto compute = [&](int kv0, int ST) {
+    const __bf16* ks = smem + ST * 2 * TILE;
+    const __bf16* vs = ks + TILE;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BC;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(j + 1);
+    // S^T for the 64 keys: two 32-key blocks, chains interleaved
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
+      s0 = mfma32(a0, qf[kc], s0);
+      s1 = mfma32(a1, qf[kc], s1);
+    }
 
-    // a wave whose rows all precede the tile's first key has nothing to do here
-    const bool active = !CAUSAL || kv0 <= wrow0 + 31;
-    if (active) {
-      const __bf16* ks = smem + (j & 1) * 2 * NP * TILE;
-      const __bf16* vs = ks + NP * TILE;
-
-      // S^T for the 64 keys: two 32-key blocks
-      f32x16 s[2];
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk);
+    if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int key = 32 * kb + sigma32(r32);
-#pragma unroll
-        for (int kc = 0; kc < KSTEPS; ++kc) {
-          const int at = key * D + 8 * ((2 * kc + half) ^ kswz(key));
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + at);
-          if constexpr (SPLIT) {
-            const bf16x8 al = *reinterpret_cast<const bf16x8*>(ks + TILE + at);
-            s[kb] = mfma32(al, qf[kc], s[kb]);
-            s[kb] = mfma32(a, ql[kc], s[kb]);
-          }
-          s[kb] = mfma32(a, qf[kc], s[kb]);
-        }
-      }
-
-      // diagonal / ragged tiles: -inf where the key is in the row's future or past the end
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            const int key = kv0 + 32 * kb + acc_key(jj, half);
-            const bool dead = (CAUSAL && key > row) || key >= nk;
-            s[kb][jj] = dead ? kNegInf : s[kb][jj];
-          }
-      }
-
-      // online softmax update for this row
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // no visible key yet
-      const float alpha = fast_exp2(m_run - m_use);           // exp2(-inf) = 0 on the first tile
-      m_run = m_new;
-
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float pv = fast_exp2(fmaf(s[kb][jj], c2, -m_use));
-          s[kb][jj] = pv;
-          rs += pv;
-        }
-      rs = half_swap_sum(rs);
-      l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
-
-      // P^T chunks of 16 keys as bf16 B operands
-      bf16x8 pb[4], pl[SPLIT ? 4 : 1];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = s[c >> 1][8 * (c & 1) + e];
-        pb[c] = to_bf16x8(f);
-        if constexpr (SPLIT) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] -= (float)pb[c][e];
-          pl[c] = to_bf16x8(f);
-        }
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d = 32 * db + r32;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int at = d * BC + 8 * ((2 * c + half) ^ vswz(d));
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + at);
-          if constexpr (SPLIT) {
-            const bf16x8 al = *reinterpret_cast<const bf16x8*>(vs + TILE + at);
-            o[db] = mfma32(al, pb[c], o[db]);
-            o[db] = mfma32(a, pl[c], o[db]);
-          }
-          o[db] = mfma32(a, pb[c], o[db]);
-        }
+      for (int jj = 0; jj < 16; ++jj) {
+        const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
+        s0[jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : s0[jj];
+        s1[jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : s1[jj];
       }
     }
 
-    if (has_next) store_tile((j + 1) & 1);
-    __syncthreads();
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(s0[jj], s1[jj]));
+    mx = half_swap_max(mx);
+    const float mt = mx * c2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {   // wave-uniform, rare
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+      l_o *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const float p0 = fast_exp2(fmaf(s0[jj], c2, -m_use));
+      const float p1 = fast_exp2(fmaf(s1[jj], c2, -m_use));
+      s0[jj] = p0;
+      s1[jj] = p1;
+      rs += p0 + p1;
+    }
+    l_run += half_swap_sum(rs);
+
+    // P^T chunks of 16 keys as bf16 B operands
+    bf16x8 pb[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[0][e] = (__bf16)s0[e];
+      pb[1][e] = (__bf16)s0[8 + e];
+      pb[2][e] = (__bf16)s1[e];
+      pb[3][e] = (__bf16)s1[8 + e];
+    }
+    float ro = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16x2 pr;
+        pr[0] = pb[c][2 * e];
+        pr[1] = pb[c][2 * e + 1];
+        ro = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ro, false);
+      }
+    l_o += half_swap_sum(ro);
+
+    // O^T += V^T P^T; V^T fragments by transposing reads (4 keys per read)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const __bf16* va = vs + voff[db] + 16 * c * D;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(va));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = mfma32(a, pb[c], o[db]);
+      }
+    }
+  };
+
+  // one pipeline step on tile j held in stage ST
+  // (called with literal stages, so after inlining every LDS address is a
+  // lane-constant register plus an immediate)
+  auto step = [&](int j, int ST) {
+    if (j >= ntiles) return;
+    if constexpr (STAGES > 2) {
+      if (j + STAGES - 2 < ntiles) wait_vmcnt<(STAGES - 2) * 2 * LPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();                 // tile j visible; stage of tile j-1 free
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, (ST + STAGES - 1) % STAGES);
+    const int kv0 = j * BC;
+    if (!CAUSAL || kv0 <= wrow0 + 31) compute(kv0, ST);   // wave-level causal skip
+  };
+
+  // prologue: the first STAGES-1 tiles in flight
+  issue(0, 0);
+  if (STAGES > 2 && 1 < ntiles) issue(1, 1 % STAGES);
+  if (STAGES > 3 && 2 < ntiles) issue(2, 2 % STAGES);
+  static_assert(STAGES <= 4, "");
+
+  for (int j = 0; j < ntiles; j += STAGES) {
+    step(j, 0);
+    step(j + 1, 1 % STAGES);
+    if constexpr (STAGES > 2) step(j + 2, 2 % STAGES);
+    if constexpr (STAGES > 3) step(j + 3, 3 % STAGES);
   }
 
   // ---- epilogue: O = acc / l (one division per row), LSE = ln 2 * (m + log2 l)
   if (row < nq) {
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
     TOut* op = reinterpret_cast<TOut*>(p.o) + b * p.o_stride[0] + hq * p.o_stride[1] + (int64_t)row * p.o_stride[2];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -313,28 +319,33 @@ __global__ __launch_bounds__(NT, min_blocks<TIn>()) void fwd_kernel(const FwdPar
   }
 }
 
-template <int D, bool CAUSAL, typename TIn, typename TOut>
+}  // namespace detail
+
+namespace {
+
+template <int D, bool CAUSAL, typename TOut, int NW, int STAGES>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const int64_t wgs = (int64_t)p.batch * p.heads_q * p.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, TIn, TOut>), dim3((unsigned)wgs), dim3(NT), 0, stream, p);
+  FwdParams q = p;
+  q.n_qtiles = (p.seqlen_q + 32 * NW - 1) / (32 * NW);
+  const int64_t wgs = (int64_t)q.batch * q.heads_q * q.n_qtiles;
+  hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, STAGES>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, q);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_io(const FwdParams& p, hipStream_t stream) {
-  if (p.in_fp32) {
-    return p.out_fp32 ? launch<D, CAUSAL, float, float>(p, stream) : launch<D, CAUSAL, float, __bf16>(p, stream);
-  }
-  return p.out_fp32 ? launch<D, CAUSAL, __bf16, float>(p, stream) : launch<D, CAUSAL, __bf16, __bf16>(p, stream);
+template <int D, bool CAUSAL, int NW, int STAGES>
+hipError_t launch_out(const FwdParams& p, hipStream_t stream) {
+  return p.out_fp32 ? launch<D, CAUSAL, float, NW, STAGES>(p, stream)
+                    : launch<D, CAUSAL, __bf16, NW, STAGES>(p, stream);
 }
 
 }  // namespace
 
-int fwd_query_tile_rows() { return BR; }
-
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
-  if (p.head_dim == 64) return p.causal ? launch_io<64, true>(p, stream) : launch_io<64, false>(p, stream);
-  return p.causal ? launch_io<128, true>(p, stream) : launch_io<128, false>(p, stream);
+  if (p.in_fp32) return launch_fwd_f32(p, stream);
+  if (p.head_dim == 64)
+    return p.causal ? launch_out<64, true, 4, 2>(p, stream) : launch_out<64, false, 4, 2>(p, stream);
+  return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream)
+                  : launch_out<128, false, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream);
 }
 
 }  // namespace fa

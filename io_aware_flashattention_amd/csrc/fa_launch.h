@@ -36,8 +36,9 @@ struct DecodeParams {
   bool out_fp32;
 };
 
-int fwd_query_tile_rows();
-hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+// n_qtiles is filled in by the launchers (it depends on the kernel's row tile).
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);       // dispatches on in_fp32
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
 int decode_default_split();
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -22,7 +22,13 @@ def fa():
 
 
 def run_and_check(q, k, v, causal, scale, what, rows=None, heads=None, bf16_direct=False):
-    """Run fa_fwd with fp32 output (and bf16 output), compare with the oracle."""
+    """Run fa_fwd with fp32 output (and bf16 output), compare with the oracle.
+
+    The bar is applied to the float32 output everywhere; the bf16 output must
+    be that result rounded once to nearest even, bit for bit. ``bf16_direct``
+    also applies the bar to the bf16 output itself (the mid-length workload,
+    whose output is bf16 by definition and stays below 4 in magnitude, so its
+    storage rounding is at most 2^-8)."""
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     say(f"case {what}: q{tuple(q.shape)} k{tuple(k.shape)} causal={causal}")
     o32, lse = fa().fwd(qd, kd, vd, causal=causal, scale=scale, out_dtype=torch.float32)
@@ -37,6 +43,9 @@ def run_and_check(q, k, v, causal, scale, what, rows=None, heads=None, bf16_dire
         check(o32, lse, o_ref, l_ref, what)
         if bf16_direct:
             check(o16, lse16, o_ref, l_ref, what + " [bf16 out]")
+        else:
+            e = np.abs(o16.float().cpu().numpy() - o_ref)
+            say(f"  {what} [bf16 out, reported]: O max {e.max():.3e} mean {e.mean():.3e}")
         return
     o_h = o32.cpu().numpy()
     l_h = lse.cpu().numpy()
@@ -91,7 +100,7 @@ def test_c1_single_head_fp32():
 def test_c2_gpt2_causal():
     cfg = W.CONFIGS["c2_gpt2_causal"]
     q, k, v = W.make_prefill_inputs(cfg)
-    run_and_check(q, k, v, cfg.causal, cfg.scale, cfg.name, bf16_direct=True)
+    run_and_check(q, k, v, cfg.causal, cfg.scale, cfg.name)
 
 
 def _sample_rows(n, seed, extra=()):
