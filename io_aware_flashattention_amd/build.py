@@ -22,11 +22,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-un
 # Packed-FP32 VALU forms are kept out of every device object.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+# The attention kernels never produce or test NaN (masked scores are -inf and
+# infinities stay honoured), so max() needs no NaN-quieting of its inputs.
+PER_SOURCE = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = PER_SOURCE.get(src, [])
+    cmd = [HIPCC, *COMMON, *extra, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, "-x", "hip", *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

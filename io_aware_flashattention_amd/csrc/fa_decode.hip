@@ -9,8 +9,9 @@
 // Paged and Split-KV Variants"; "FlashAttention and GPU Data Movement",
 // section 6.1).
 //
-// Work item = (sequence b, kv head, split s), one wave each, four per
-// workgroup. All G query heads of the kv head are processed together, so each
+// Work item = (sequence b, kv head, split s), one wave each; a workgroup is
+// one wave by default, so a workgroup whose split lies past a short
+// sequence's end exits at once and holds no LDS. All G query heads of the kv head are processed together, so each
 // cached K/V byte is read from memory exactly once. Per 32-key block the wave
 //   * loads 8 KB of K and 8 KB of V with fully coalesced 16-byte loads (the
 //     next block's loads are issued before the current block is computed),
@@ -27,18 +28,25 @@ namespace fa {
 
 namespace {
 
+#ifndef FA_DEC_WAVES
+#define FA_DEC_WAVES 1       // independent work items (waves) per workgroup
+#endif
+#ifndef FA_DEC_SPLIT
+#define FA_DEC_SPLIT 1024    // default keys per split
+#endif
+
 constexpr int D = 128;
 constexpr int KB = 32;                 // keys per block
-constexpr int WAVES = 4;
+constexpr int WAVES = FA_DEC_WAVES;
 constexpr int NT = 64 * WAVES;
-constexpr int DEFAULT_SPLIT = 1024;
+constexpr int DEFAULT_SPLIT = FA_DEC_SPLIT;
 
 // Vt rows are 32 keys (64 bytes, four 16-byte chunks); the XOR keeps both the
 // fragment reads (8 consecutive d rows) and the transposing writes spread.
 __device__ __forceinline__ int vswz32(int d) { return ((d >> 1) & 3) ^ ((d >> 3) & 3); }
 
 template <typename TOut>
-__global__ __launch_bounds__(NT, 2) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(const DecodeParams p) {
   constexpr int DCH = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;

@@ -51,10 +51,21 @@ namespace {
 constexpr int BC = 64;       // keys per tile
 constexpr float kRescaleThreshold = 8.f;
 
-// V tile swizzle for the transposing reads: a 16-lane group reads 4
-// consecutive rows x 32 bytes; XOR-ing the 16-byte chunk index by 2*(row%4)
-// puts the 4 rows on disjoint bank groups.
-__device__ __forceinline__ int vswz_tr(int r) { return 2 * (r & 3); }
+// LDS swizzles, measured against gfx950's 64 banks x 4 bytes: a ds_read_b128
+// is served 16 lanes at a time and a ds_read_b64_tr_b16 32 lanes at a time;
+// either is conflict-free when those lanes hit 16 distinct 16-byte slots of a
+// 256-byte bank line. XOR patterns on the 16-byte chunk index of a row:
+//   K (fragment rows sigma(0..15) at one chunk): D = 128 rows are 256 bytes,
+//     so the chunk is XOR-ed with sigma(row) & 15 (= the lane number); D = 64
+//     rows are 128 bytes (two rows per bank line), XOR with (row >> 1) & 7;
+//   V (transposing reads: 4 consecutive rows x 64 bytes per 32 lanes): XOR
+//     with 4 * (row % 4) for D = 128 and 4 * ((row >> 1) % 2) for D = 64.
+template <int D> __device__ __forceinline__ int kswz_t(int r) {
+  return D == 128 ? (sigma32(r & 31) & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int vswz_t(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // LDS pointer type for the direct global -> LDS loads (the host pass of the
 // compiler needs the address space spelled out).
@@ -126,8 +137,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
     const int byte = (wave * LPW + i) * 1024 + lane * 16;
     const int r = byte / ROWB, pc = (byte % ROWB) / 16;
     dma_row[i] = r;
-    dma_k[i] = 8 * (pc ^ kswz(r));
-    dma_v[i] = 8 * (pc ^ vswz_tr(r));
+    dma_k[i] = 8 * (pc ^ kswz_t<D>(r));
+    dma_v[i] = 8 * (pc ^ vswz_t<D>(r));
   }
   auto issue = [&](int tile, int ST) {
     const int kv0 = tile * BC;
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
   {
     const int r = sigma32(r32);
 #pragma unroll
-    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz(r));
+    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz_t<D>(r));
   }
   int voff[DBLK];
   {
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
-      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_tr(r)) + (col & 7);
+      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_t<D>(r)) + (col & 7);
     }
   }
 
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
       }
     }
 
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = fmaxf(s0[0], s1[0]);          // three-input max chain (v_max3_f32)
 #pragma unroll
     for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(s0[jj], s1[jj]));
     mx = half_swap_max(mx);
