@@ -99,12 +99,13 @@ FA_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, 
                    float softmax_scale, void* stream);
 
 /*
- * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes
- * (per-split partial outputs and log-sum-exps, float32). split_tokens <= 0
- * selects the library default. Returns 0 for invalid sizes.
+ * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes:
+ * float32 partial outputs and log-sum-exps, one set of heads_q/heads_kv heads
+ * per piece of work (at most batch*heads_kv plus the decode grid's size).
+ * Returns 0 for invalid sizes.
  */
-FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
-                                 int32_t head_dim, int32_t split_tokens);
+FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t max_seqlen_k, int32_t head_dim);
 
 /*
  * fa_decode -- one query token per sequence against a contiguous KV cache.
@@ -118,16 +119,20 @@ FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t 
  *          and LSE = -inf for that sequence.
  * o        [batch, heads_q, head_dim] out_dtype, contiguous
  * lse      [batch, heads_q] float32, contiguous; may be NULL.
- * split_tokens  keys per split (multiple of 64); <= 0 selects the default.
- *          LSE does not depend on it beyond float32 rounding; O may move by
- *          bf16 rounding of the probabilities, which each split takes relative
- *          to its own running maximum.
+ * split_tokens  the cached rows of all sequences are cut into equal contiguous
+ *          ranges, one per workgroup of a fixed grid; split_tokens > 0 is a
+ *          lower bound on the keys of one range, <= 0 leaves the ranges as even
+ *          as the grid allows. LSE does not depend on it beyond float32
+ *          rounding; O may move by the bf16 rounding of the probabilities,
+ *          which each range takes relative to its own running maximum.
  * workspace      device buffer of at least fa_decode_workspace_bytes(...) bytes,
  *          16-byte aligned; its contents on entry do not matter and are
  *          overwritten. Two calls that share a workspace must be ordered.
  *
  * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
  * bf16 q and cache; pointers 16-byte aligned; kv strides multiples of 8.
+ * Every cache row a sequence may read (index < its length) must lie inside
+ * the caches; rows at or past a sequence's length are never read.
  */
 FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seqlens_k, void* o, float* lse,

@@ -47,7 +47,7 @@ def load():
                            _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                            ctypes.c_float, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
-    lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
                               ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
@@ -113,8 +113,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return out, lse
 
 
-def decode_workspace_bytes(batch: int, heads_q: int, max_seqlen: int, head_dim: int, split_tokens: int = 0) -> int:
-    return int(load().fa_decode_workspace_bytes(batch, heads_q, max_seqlen, head_dim, split_tokens))
+def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seqlen: int, head_dim: int) -> int:
+    return int(load().fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim))
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
@@ -139,7 +139,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     elif lse is False:
         lse = None
-    need = decode_workspace_bytes(B, Hq, Lmax, d, split_tokens)
+    need = decode_workspace_bytes(B, Hq, Hkv, Lmax, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),

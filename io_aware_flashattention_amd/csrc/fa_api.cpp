@@ -132,12 +132,13 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return ok();
 }
 
-size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
-                                 int32_t head_dim, int32_t split_tokens) {
-  if (batch <= 0 || heads_q <= 0 || max_seqlen_k <= 0 || head_dim <= 0) return 0;
-  const int split = split_tokens > 0 ? split_tokens : fa::decode_default_split();
-  const int64_t splits = (max_seqlen_k + split - 1) / split;
-  return static_cast<size_t>((int64_t)batch * heads_q * splits * (head_dim + 1) * 4);
+size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                 int32_t max_seqlen_k, int32_t head_dim) {
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || max_seqlen_k <= 0 || head_dim <= 0) return 0;
+  if (heads_q % heads_kv != 0) return 0;
+  // one partial (G heads x (d + 1) floats) per (slab, wave) piece: at most B*Hkv + W
+  const int64_t parts = (int64_t)batch * heads_kv + fa::decode_waves();
+  return static_cast<size_t>(parts * (heads_q / heads_kv) * (head_dim + 1) * 4);
 }
 
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -160,27 +161,26 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head",
                 heads_q, heads_kv);
-  const int split = split_tokens > 0 ? split_tokens : fa::decode_default_split();
-  if (split % 64 != 0) return fail(FA_ERR_UNSUPPORTED, "fa_decode: split_tokens (%d) must be a multiple of 64", split);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
     return fail(FA_ERR_UNSUPPORTED, "fa_decode: q, caches, o and workspace must be 16-byte aligned");
   for (int i = 0; i < 3; ++i)
     if (kv_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "fa_decode: kv strides must be multiples of 8 elements");
-  const size_t need = fa_decode_workspace_bytes(batch, heads_q, max_seqlen_k, head_dim, split);
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen_k, head_dim);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  const int64_t splits = (max_seqlen_k + split - 1) / split;
-  if ((int64_t)batch * heads_kv * splits / 4 + 1 > 0x7fffffffLL)
+  if ((int64_t)batch * heads_q > 0x7fffffffLL / 4)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode: problem too large for one launch");
 
   fa::DecodeParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.seqlens = seqlens_k; p.o = o; p.lse = lse;
+  const int64_t parts = ((int64_t)batch * heads_kv + fa::decode_waves()) * (heads_q / heads_kv);
   p.part_o = static_cast<float*>(workspace);
-  p.part_lse = p.part_o + (int64_t)batch * heads_q * splits * head_dim;
+  p.part_lse = p.part_o + parts * head_dim;
   for (int i = 0; i < 3; ++i) p.kv_stride[i] = kv_stride[i];
   p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
   p.max_seqlen = max_seqlen_k; p.head_dim = head_dim;
-  p.split_tokens = split; p.max_splits = (int)splits;
+  p.split_tokens = split_tokens > 0 ? split_tokens : 0;
+  p.n_waves = fa::decode_waves();
   p.scale_log2 = softmax_scale * kLog2e;
   p.out_fp32 = out_dtype == FA_DTYPE_FP32;
   hipError_t e = fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream));

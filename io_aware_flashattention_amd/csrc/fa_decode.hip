@@ -1,159 +1,254 @@
 // Split-KV single-token decode for gfx950.
 //
 // With one query token per sequence the query-tile axis collapses to a single
-// tile, so the key axis is the only long one: it is cut into splits of
-// `split_tokens` keys, every split computes a partial output and its
-// log-sum-exp, and a small second kernel merges the partials with the same
-// rescaling identity the tile loop uses ("FlashAttention Explained: IO-Aware
-// Attention, Tiling, Online Softmax and FP8 on Hopper", section "Decoding,
-// Paged and Split-KV Variants"; "FlashAttention and GPU Data Movement",
-// section 6.1).
+// tile, so the key axis is the only long one: it is split across workgroups,
+// every piece computes a partial output and its log-sum-exp, and a small
+// second kernel merges the partials with the same rescaling identity the tile
+// loop uses ("FlashAttention Explained: IO-Aware Attention, Tiling, Online
+// Softmax and FP8 on Hopper", section "Decoding, Paged and Split-KV
+// Variants"; "FlashAttention and GPU Data Movement", section 6.1).
 //
-// Work item = (sequence b, kv head, split s), one wave each; a workgroup is
-// one wave by default, so a workgroup whose split lies past a short
-// sequence's end exits at once and holds no LDS. All G query heads of the kv head are processed together, so each
-// cached K/V byte is read from memory exactly once. Per 32-key block the wave
-//   * loads 8 KB of K and 8 KB of V with fully coalesced 16-byte loads (the
-//     next block's loads are issued before the current block is computed),
-//   * re-lays them through a wave-private LDS region (K as [key][d], V
-//     transposed as [d][key], XOR-swizzled chunks),
+// Work split (balanced by construction). The cache rows to read form one
+// stream of T = Hkv * sum_b L_b tokens, slab after slab, slab = (sequence b,
+// kv head). A fixed grid of W one-wave workgroups cuts it into W equal
+// contiguous ranges of P tokens (P >= split_tokens). A wave streams its range
+// and emits a partial (o, lse) for the G query heads of a slab each time it
+// finishes its piece of that slab; the piece of slab s done by wave w is
+// stored at index s + w, so at most B*Hkv + W partials exist. Every wave reads
+// the same number of bytes, whatever the mix of sequence lengths.
+//
+// Per 32-key block the wave
+//   * moves 8 KB of K and 8 KB of V global -> LDS with direct DMA loads into
+//     a private ring of NST stages, NST-1 blocks ahead of the compute;
 //   * computes S^T = K q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with
-//     the G heads on the N axis (the kernel is bound by memory, not by the
-//     matrix cores, so the padding of N to 32 costs nothing that matters),
-//   * updates the running max / sum of each head (one lane per head).
+//     the G heads of the kv head on the N axis (bound by memory, not by the
+//     matrix cores), K fragments by ds_read_b128 and V^T fragments by
+//     transposing ds_read_b64_tr_b16, both through conflict-free swizzles;
+//   * updates each head's running max and sums (one lane per head), with the
+//     accumulator rescaled only when a maximum grows by more than 2^8; O is
+//     normalised by the sum of the bf16-rounded weights, the log-sum-exp uses
+//     the float32 sum.
 #include "fa_device.h"
 #include "fa_launch.h"
+
+#ifndef FA_DEC_NST
+#define FA_DEC_NST 3          // ring stages per wave (NST-1 blocks in flight)
+#endif
+#ifndef FA_DEC_WPC
+#define FA_DEC_WPC 3          // one-wave workgroups per CU (LDS-limited)
+#endif
 
 namespace fa {
 
 namespace {
 
-#ifndef FA_DEC_WAVES
-#define FA_DEC_WAVES 1       // independent work items (waves) per workgroup
-#endif
-#ifndef FA_DEC_SPLIT
-#define FA_DEC_SPLIT 1024    // default keys per split
-#endif
-
 constexpr int D = 128;
-constexpr int KB = 32;                 // keys per block
-constexpr int WAVES = FA_DEC_WAVES;
-constexpr int NT = 64 * WAVES;
-constexpr int DEFAULT_SPLIT = FA_DEC_SPLIT;
+constexpr int KB = 32;                       // keys per block
+constexpr int NST = FA_DEC_NST;
+constexpr int BLK = KB * D;                  // bf16 elements per K (or V) block
+constexpr float kRescaleThreshold = 8.f;
+static_assert(NST >= 2 && NST <= 4, "");
 
-// Vt rows are 32 keys (64 bytes, four 16-byte chunks); the XOR keeps both the
-// fragment reads (8 consecutive d rows) and the transposing writes spread.
-__device__ __forceinline__ int vswz32(int d) { return ((d >> 1) & 3) ^ ((d >> 3) & 3); }
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// swizzles of 256-byte rows (the bank model is described with the prefill kernel)
+__device__ __forceinline__ int kswz_d(int r) { return sigma32(r & 31) & 15; }
+__device__ __forceinline__ int vswz_d(int r) { return 4 * (r & 3); }
+
+__device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
+  return min(max(p.seqlens[b], 0), p.max_seqlen);
+}
+
+// Tokens per wave range, identical in both kernels: at least split_tokens, a
+// multiple of the block, and W ranges cover all T tokens of the stream.
+__device__ __forceinline__ int64_t range_tokens(const DecodeParams& p, int64_t T) {
+  int64_t P = (T + p.n_waves - 1) / p.n_waves;
+  P = P > p.split_tokens ? P : p.split_tokens;
+  return (P + KB - 1) / KB * KB;
+}
+
+// Position in the token stream: slab (b, kvh), key position inside the slab
+// and end of the current piece (exclusive, inside the slab).
+struct Cursor {
+  int b, kvh, pos, end;
+  int64_t slab_off;          // stream offset of the slab's first token
+};
+
+}  // namespace
+
+namespace detail {
 
 template <typename TOut>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(const DecodeParams p) {
-  constexpr int DCH = D / 8;
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[WAVES][2 * KB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[NST * 2 * BLK];      // [stage][K, V][BLK]
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int half = lane >> 5;
   const int r32 = lane & 31;
-
-  const int64_t item = (int64_t)blockIdx.x * WAVES + wave;
-  const int s = (int)(item % p.max_splits);
-  const int64_t bh = item / p.max_splits;
-  if (bh >= (int64_t)p.batch * p.heads_kv) return;
-  const int kvh = (int)(bh % p.heads_kv);
-  const int b = (int)(bh / p.heads_kv);
-  const int len = min(max(p.seqlens[b], 0), p.max_seqlen);
-  const int k_begin = s * p.split_tokens;
-  if (k_begin >= len) return;                     // this split holds no key
-  const int k_end = min(len, k_begin + p.split_tokens);
-
-  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
-  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
+  const int w = blockIdx.x;
   const int G = p.group;
-  const int head = kvh * G + r32;                 // this lane's query head (valid if r32 < G)
+  const int Hkv = p.heads_kv;
 
-  // query of this lane's head as B-operand fragments (heads past G are zero)
-  bf16x8 qf[KSTEPS];
+  // ---- plan: stream length and this wave's range [r0, r1)
+  int64_t T = 0;
+  for (int b = 0; b < p.batch; ++b) T += (int64_t)seq_len(p, b);
+  T *= Hkv;
+  const int64_t P = range_tokens(p, T);
+  const int64_t r0 = (int64_t)w * P;
+  if (r0 >= T) return;
+  const int64_t r1 = r0 + P < T ? r0 + P : T;
+
+  Cursor cur;                                // slab holding r0
   {
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + ((int64_t)b * p.heads_q + head) * D;
+    int64_t off = 0;
+    int b = 0;
+    for (;; ++b) {
+      const int64_t n = (int64_t)seq_len(p, b) * Hkv;
+      if (r0 < off + n) break;
+      off += n;
+    }
+    const int L = seq_len(p, b);
+    const int kvh = (int)((r0 - off) / L);
+    cur.b = b;
+    cur.kvh = kvh;
+    cur.slab_off = off + (int64_t)kvh * L;
+    cur.pos = (int)(r0 - cur.slab_off);
+    cur.end = (int)min((int64_t)L, r1 - cur.slab_off);
+  }
+  // one block further along the range; false once it is exhausted
+  auto advance = [&](Cursor& c) -> bool {
+    c.pos += KB;
+    if (c.pos < c.end) return true;
+    if (c.slab_off + c.end >= r1) return false;
+    int L = seq_len(p, c.b);
+    c.slab_off += L;
+    if (++c.kvh == Hkv) {                      // next non-empty sequence
+      c.kvh = 0;
+      do {
+        ++c.b;
+        L = seq_len(p, c.b);
+      } while (L == 0);
+    }
+    c.pos = 0;
+    c.end = (int)min((int64_t)L, r1 - c.slab_off);
+    return true;
+  };
+
+  // ---- DMA of one block: eight 1-KB writes per operand, rows past the piece clamped
+  const int drow = lane >> 4;                  // row of the lane's chunk, + 4 per write
+  const int dchunk = lane & 15;
+  auto issue = [&](const Cursor& c, int st) {
+    const int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
+    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + base;
+    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + base;
+    const int last = c.end - 1;
 #pragma unroll
-    for (int kc = 0; kc < KSTEPS; ++kc)
-      qf[kc] = as_bf16x8(r32 < G ? load16(qp + 16 * kc + 8 * half) : u32x4{0, 0, 0, 0});
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + drow;
+      const int key = min(c.pos + r, last);
+      __bf16* dk = smem + st * 2 * BLK + i * 512;
+      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * p.kv_stride[2] + 8 * (dchunk ^ kswz_d(r))),
+                                       (lds_void*)dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)key * p.kv_stride[2] + 8 * (dchunk ^ vswz_d(r))),
+                                       (lds_void*)(dk + BLK), 16, 0, 0);
+    }
+  };
+
+  // ---- lane-constant fragment offsets (elements)
+  int koff[KSTEPS];
+  {
+    const int r = sigma32(r32);
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz_d(r));
+  }
+  int voff[DBLK];
+  {
+    const int gg = lane >> 4, i = lane & 15;
+    const int r = 8 * (gg >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
+      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_d(r)) + (col & 7);
+    }
   }
 
-  __bf16* ks = smem[wave];
-  __bf16* vs = ks + KB * D;
-
-  // lane's share of a 32-key block: keys 8*kg + i (i = 0..7) of d-chunk dc
-  const int dc = lane % DCH, kg = lane / DCH;
-  u32x4 kreg[8], vreg[8];
-  auto load_block = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = k0 + 8 * kg + i;
-      const bool ok = key < k_end;
-      kreg[i] = ok ? load16(kp + (int64_t)key * p.kv_stride[2] + 8 * dc) : u32x4{0, 0, 0, 0};
-      vreg[i] = ok ? load16(vp + (int64_t)key * p.kv_stride[2] + 8 * dc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = 8 * kg + i;
-      *reinterpret_cast<u32x4*>(ks + key * D + 8 * (dc ^ kswz(key))) = kreg[i];
-    }
-    // element e of keys 8kg..8kg+7 -> Vt[8*dc + e][8kg .. 8kg+7]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      uint32_t w[4];
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const uint32_t lo = (vreg[2 * i2][e >> 1] >> sh) & 0xffffu;
-        const uint32_t hi = (vreg[2 * i2 + 1][e >> 1] >> sh) & 0xffffu;
-        w[i2] = lo | (hi << 16);
-      }
-      const int d = 8 * dc + e;
-      *reinterpret_cast<u32x4*>(vs + d * KB + 8 * (kg ^ vswz32(d))) = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  };
-
   const float c2 = p.scale_log2;
-  float m_run = kNegInf, l_run = 0.f;
+  bf16x8 qf[KSTEPS];
+  int q_b = -1, q_kvh = -1;
+  float m_run = kNegInf, l_run = 0.f, l_o = 0.f;
   f32x16 o[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
 
-  load_block(k_begin);
-  for (int k0 = k_begin; k0 < k_end; k0 += KB) {
-    store_block();
-    if (k0 + KB < k_end) load_block(k0 + KB);      // in flight while this block computes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // prologue: NST-1 blocks in flight
+  Cursor dma = cur;
+  bool dma_ok = true;
+  int issued = 0;
+  for (int s = 0; s < NST - 1 && dma_ok; ++s) {
+    issue(dma, s);
+    ++issued;
+    dma_ok = advance(dma);
+  }
 
-    f32x16 sc = f32x16{};
-    {
-      const int key = sigma32(r32);
-#pragma unroll
-      for (int kc = 0; kc < KSTEPS; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + key * D + 8 * ((2 * kc + half) ^ kswz(key)));
-        sc = mfma32(a, qf[kc], sc);
-      }
+  for (int blk = 0;; ++blk) {
+    const int st = blk % NST;
+    if (dma_ok) {                              // refill the stage block blk-1 used
+      issue(dma, (blk + NST - 1) % NST);
+      ++issued;
+      dma_ok = advance(dma);
     }
-    if (k0 + KB > k_end) {
+    const int ahead = issued - blk - 1;        // blocks allowed to stay in flight
+    if (ahead >= 3) wait_vmcnt<48>();
+    else if (ahead == 2) wait_vmcnt<32>();
+    else if (ahead == 1) wait_vmcnt<16>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (cur.b != q_b || cur.kvh != q_kvh) {    // this slab's queries as B operands
+      q_b = cur.b;
+      q_kvh = cur.kvh;
+      const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + ((int64_t)q_b * p.heads_q + q_kvh * G + r32) * D;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) sc[jj] = (k0 + acc_key(jj, half) >= k_end) ? kNegInf : sc[jj];
+      for (int kc = 0; kc < KSTEPS; ++kc)
+        qf[kc] = as_bf16x8(r32 < G ? load16(qp + 16 * kc + 8 * half) : u32x4{0, 0, 0, 0});
+    }
+
+    const __bf16* ks = smem + st * 2 * BLK;
+    const __bf16* vs = ks + BLK;
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc)
+      sc = mfma32(*reinterpret_cast<const bf16x8*>(ks + koff[kc]), qf[kc], sc);
+    const int valid = cur.end - cur.pos;       // keys of this block inside the piece
+    if (valid < KB) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) sc[jj] = acc_key(jj, half) >= valid ? kNegInf : sc[jj];
     }
     float mx = sc[0];
 #pragma unroll
     for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[jj]);
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    const float mt = half_swap_max(mx) * c2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+      l_o *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -161,95 +256,128 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       sc[jj] = pv;
       rs += pv;
     }
-    rs = half_swap_sum(rs);
-    l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
     bf16x8 pb[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = sc[8 * c + e];
-      pb[c] = to_bf16x8(f);
+    for (int e = 0; e < 8; ++e) {
+      pb[0][e] = (__bf16)sc[e];
+      pb[1][e] = (__bf16)sc[8 + e];
     }
+    float ro = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const int d = 32 * db + r32;
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + d * KB + 8 * ((2 * c + half) ^ vswz32(d)));
-        o[db] = mfma32(a, pb[c], o[db]);
+      for (int e = 0; e < 4; ++e) {
+        bf16x2 pr;
+        pr[0] = pb[c][2 * e];
+        pr[1] = pb[c][2 * e + 1];
+        ro = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ro, false);
       }
-    }
-    // the next store_block overwrites this wave's LDS: keep the reads first
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+    l_run += half_swap_sum(rs);
+    l_o += half_swap_sum(ro);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const __bf16* va = vs + voff[db] + 16 * c * D;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
+        o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[c], o[db]);
+      }
 
-  // partial of this split: normalised output and its log-sum-exp
-  if (r32 < G) {
-    const float inv_l = 1.f / l_run;                // l_run >= 1: the split holds a key
-    float* po = p.part_o + (((int64_t)b * p.heads_q + head) * p.max_splits + s) * D;
+    // end of a piece: its partial for the G heads goes to index slab + w
+    if (cur.pos + KB >= cur.end) {
+      const int slab = cur.b * Hkv + cur.kvh;
+      if (r32 < G) {
+        const int64_t part = (int64_t)(slab + w) * G + r32;
+        const float inv = 1.f / l_o;           // l_o >= 1: the piece holds a key
+        float* po = p.part_o + part * D;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+        for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * half;
-        *reinterpret_cast<f32x4*>(po + d) = f32x4{o[db][4 * gq] * inv_l, o[db][4 * gq + 1] * inv_l,
-                                                  o[db][4 * gq + 2] * inv_l, o[db][4 * gq + 3] * inv_l};
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d = 32 * db + 8 * gq + 4 * half;
+            *reinterpret_cast<f32x4*>(po + d) = f32x4{o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
+                                                      o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv};
+          }
+        if (half == 0) p.part_lse[part] = (m_run + __log2f(l_run)) * kLn2;
       }
-    if (half == 0)
-      p.part_lse[((int64_t)b * p.heads_q + head) * p.max_splits + s] = (m_run + __log2f(l_run)) * kLn2;
+      m_run = kNegInf;
+      l_run = 0.f;
+      l_o = 0.f;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+    }
+    wait_lgkm0();                              // this stage's reads are done before it is refilled
+    __builtin_amdgcn_sched_barrier(0);
+    if (!advance(cur)) break;
   }
 }
 
-// One wave per (b, query head): LSE = log sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) o_s.
+// One wave per (b, query head): LSE = log sum_s exp(lse_s), O = sum_s
+// exp(lse_s - LSE) o_s over the pieces s of the head's slab.
 template <typename TOut>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)p.batch * p.heads_q) return;
   const int b = (int)(row / p.heads_q);
-  const int len = min(max(p.seqlens[b], 0), p.max_seqlen);
-  const int ns = (len + p.split_tokens - 1) / p.split_tokens;
-  const float* pl = p.part_lse + row * p.max_splits;
-  const float* po = p.part_o + row * p.max_splits * D;
-  float mx = kNegInf;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, pl[s]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  if (ns > 0) {
-    for (int s = 0; s < ns; ++s) {
-      const float w = __expf(pl[s] - mx);
-      const float2 v = *reinterpret_cast<const float2*>(po + (int64_t)s * D + 2 * lane);
-      den += w;
-      n0 = fmaf(w, v.x, n0);
-      n1 = fmaf(w, v.y, n1);
-    }
+  const int hq = (int)(row % p.heads_q);
+  const int G = p.group;
+  const int kvh = hq / G, g = hq % G;
+  int64_t T = 0, before = 0;
+  for (int bb = 0; bb < p.batch; ++bb) {
+    const int64_t n = seq_len(p, bb);
+    if (bb < b) before += n;
+    T += n;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  T *= p.heads_kv;
+  const int L = seq_len(p, b);
   TOut* op = reinterpret_cast<TOut*>(p.o) + row * D + 2 * lane;
+  if (L == 0) {                                // no key: O = 0, LSE = -inf
+    op[0] = (TOut)0.f;
+    op[1] = (TOut)0.f;
+    if (p.lse != nullptr && lane == 0) p.lse[row] = kNegInf;
+    return;
+  }
+  const int64_t P = range_tokens(p, T);
+  const int64_t slab_off = before * p.heads_kv + (int64_t)kvh * L;
+  const int w0 = (int)(slab_off / P), w1 = (int)((slab_off + L - 1) / P);
+  const int slab = b * p.heads_kv + kvh;
+  float mx = kNegInf;
+  for (int w = w0; w <= w1; ++w) mx = fmaxf(mx, p.part_lse[(int64_t)(slab + w) * G + g]);
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  for (int w = w0; w <= w1; ++w) {
+    const int64_t part = (int64_t)(slab + w) * G + g;
+    const float wt = __expf(p.part_lse[part] - mx);
+    const float2 v = *reinterpret_cast<const float2*>(p.part_o + part * D + 2 * lane);
+    den += wt;
+    n0 = fmaf(wt, v.x, n0);
+    n1 = fmaf(wt, v.y, n1);
+  }
+  const float inv = 1.f / den;
   op[0] = (TOut)(n0 * inv);
   op[1] = (TOut)(n1 * inv);
-  if (p.lse != nullptr && lane == 0) p.lse[row] = den > 0.f ? mx + __logf(den) : kNegInf;
+  if (p.lse != nullptr && lane == 0) p.lse[row] = mx + __logf(den);
 }
+
+}  // namespace detail
+
+namespace {
 
 template <typename TOut>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.batch * p.heads_kv * p.max_splits;
-  const int64_t wgs = (items + WAVES - 1) / WAVES;
-  hipLaunchKernelGGL((decode_split_kernel<TOut>), dim3((unsigned)wgs), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((detail::decode_split_kernel<TOut>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.heads_q;
-  hipLaunchKernelGGL((decode_merge_kernel<TOut>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((detail::decode_merge_kernel<TOut>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_default_split() { return DEFAULT_SPLIT; }
+int decode_waves() { return 256 * FA_DEC_WPC; }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   return p.out_fp32 ? launch_t<float>(p, stream) : launch_t<__bf16>(p, stream);

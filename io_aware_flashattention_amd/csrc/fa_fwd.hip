@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
   constexpr int NLD = TILE * 2 / 1024;       // 1-KB DMA writes per operand tile
   constexpr int LPW = NLD / NW;              // of those, per wave
   static_assert(NLD % NW == 0, "tile / wave mismatch");
-  static_assert(STAGES >= 2, "");
+  static_assert(STAGES == 3, "the software pipeline keeps tiles j, j+1 and j+2 in LDS");
 
   __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE];   // [stage][K, V][TILE]
 
@@ -185,36 +185,45 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
 
-  auto compute = [&](int kv0, int ST) {
-    const __bf16* ks = smem + ST * 2 * TILE;
-    const __bf16* vs = ks + TILE;
+  // tiles this wave needs (under the causal mask, the rest lie in its future)
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : ntiles;
 
-    // S^T for the 64 keys: two 32-key blocks, chains interleaved
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // S^T of one 64-key tile (K in stage ST): two 32-key blocks, chains interleaved
+  auto scores = [&](int ST, f32x16& a0, f32x16& a1) {
+    const __bf16* ks = smem + ST * 2 * TILE;
+    a0 = f32x16{};
+    a1 = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KSTEPS; ++kc) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
-      s0 = mfma32(a0, qf[kc], s0);
-      s1 = mfma32(a1, qf[kc], s1);
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
+      a0 = mfma32(k0, qf[kc], a0);
+      a1 = mfma32(k1, qf[kc], a1);
     }
+  };
 
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk);
-    if (need_mask) {
+  // diagonal / ragged tiles: -inf where the key is in the row's future or past the end
+  auto mask = [&](int kv0, f32x16& a0, f32x16& a1) {
+    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
-        s0[jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : s0[jj];
-        s1[jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : s1[jj];
+        a0[jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : a0[jj];
+        a1[jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : a1[jj];
       }
     }
+  };
 
-    float mx = fmaxf(s0[0], s1[0]);          // three-input max chain (v_max3_f32)
+  // row maximum of a tile; moves the base (rescaling O and the sums) only when
+  // some row's maximum grows by more than the threshold (wave-uniform, rare)
+  auto row_max = [&](const f32x16& a0, const f32x16& a1) {
+    float mx = fmaxf(a0[0], a1[0]);          // three-input max chain (v_max3_f32)
 #pragma unroll
-    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(s0[jj], s1[jj]));
-    mx = half_swap_max(mx);
-    const float mt = mx * c2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {   // wave-uniform, rare
+    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(a0[jj], a1[jj]));
+    return half_swap_max(mx) * c2;
+  };
+  auto move_base = [&](float mt) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
       l_run *= alpha;
@@ -223,27 +232,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
       m_run = m_new;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
+  };
 
+  // weights of a tile against the current base: float32 and bf16 row sums,
+  // bf16 P^T chunks of 16 keys as B operands
+  auto weights = [&](f32x16& a0, f32x16& a1, bf16x8 (&pb)[4]) {
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const float p0 = fast_exp2(fmaf(s0[jj], c2, -m_use));
-      const float p1 = fast_exp2(fmaf(s1[jj], c2, -m_use));
-      s0[jj] = p0;
-      s1[jj] = p1;
+      const float p0 = fast_exp2(fmaf(a0[jj], c2, -m_use));
+      const float p1 = fast_exp2(fmaf(a1[jj], c2, -m_use));
+      a0[jj] = p0;
+      a1[jj] = p1;
       rs += p0 + p1;
     }
-    l_run += half_swap_sum(rs);
-
-    // P^T chunks of 16 keys as bf16 B operands
-    bf16x8 pb[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[0][e] = (__bf16)s0[e];
-      pb[1][e] = (__bf16)s0[8 + e];
-      pb[2][e] = (__bf16)s1[e];
-      pb[3][e] = (__bf16)s1[8 + e];
+      pb[0][e] = (__bf16)a0[e];
+      pb[1][e] = (__bf16)a0[8 + e];
+      pb[2][e] = (__bf16)a1[e];
+      pb[3][e] = (__bf16)a1[8 + e];
     }
     float ro = 0.f;
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -256,9 +265,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
         pr[1] = pb[c][2 * e + 1];
         ro = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ro, false);
       }
+    l_run += half_swap_sum(rs);
     l_o += half_swap_sum(ro);
+  };
 
-    // O^T += V^T P^T; V^T fragments by transposing reads (4 keys per read)
+  // O^T += V^T P^T (V in stage ST); V^T fragments by transposing reads, 4 keys each
+  auto accumulate = [&](int ST, const bf16x8 (&pb)[4]) {
+    const __bf16* vs = smem + ST * 2 * TILE + TILE;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -274,34 +287,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
     }
   };
 
-  // one pipeline step on tile j held in stage ST
-  // (called with literal stages, so after inlining every LDS address is a
-  // lane-constant register plus an immediate)
-  auto step = [&](int j, int ST) {
+  // Software pipeline over tiles. Iteration j holds tile j (V) and tile j+1
+  // (K) in LDS and loads tile j+2: the scores of tile j+1 go to the matrix
+  // cores while the exponentials of tile j run on the vector ALUs, then
+  // O += V_j P_j overlaps the row maximum of tile j+1.
+  f32x16 c0, c1;                    // scores of tile j (the current tile)
+  issue(0, 0);
+  if (1 < ntiles) issue(1, 1);
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (0 < nt_w) {
+    scores(0, c0, c1);
+    mask(0, c0, c1);
+    move_base(row_max(c0, c1));
+  }
+
+  auto step = [&](int j, int SV) {          // SV = j % 3: stage of tile j
     if (j >= ntiles) return;
-    if constexpr (STAGES > 2) {
-      if (j + STAGES - 2 < ntiles) wait_vmcnt<(STAGES - 2) * 2 * LPW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
+    const int SK = (SV + 1) % 3;             // stage of tile j+1
+    if (j > 0) {
+      wait_vmcnt<0>();                       // tile j+1 landed (this wave's share)
+      __syncthreads();                       // ... everyone's; tile j-1's stage is free
     }
-    __syncthreads();                 // tile j visible; stage of tile j-1 free
-    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, (ST + STAGES - 1) % STAGES);
-    const int kv0 = j * BC;
-    if (!CAUSAL || kv0 <= wrow0 + 31) compute(kv0, ST);   // wave-level causal skip
+    if (j + 2 < ntiles) issue(j + 2, (SV + 2) % 3);
+    const bool cur = j < nt_w, nxt = j + 1 < nt_w;
+    bf16x8 pb[4];
+    f32x16 n0, n1;
+    if (cur && nxt) {
+      scores(SK, n0, n1);                    // matrix cores ...
+      weights(c0, c1, pb);                   // ... alongside the exponentials
+      mask((j + 1) * BC, n0, n1);
+      accumulate(SV, pb);                    // matrix cores ...
+      const float mt = row_max(n0, n1);      // ... alongside the next maximum
+      move_base(mt);
+      c0 = n0;
+      c1 = n1;
+    } else if (cur) {                        // this wave's last tile
+      weights(c0, c1, pb);
+      accumulate(SV, pb);
+    }
   };
 
-  // prologue: the first STAGES-1 tiles in flight
-  issue(0, 0);
-  if (STAGES > 2 && 1 < ntiles) issue(1, 1 % STAGES);
-  if (STAGES > 3 && 2 < ntiles) issue(2, 2 % STAGES);
-  static_assert(STAGES <= 4, "");
-
-  for (int j = 0; j < ntiles; j += STAGES) {
+  for (int j = 0; j < ntiles; j += 3) {
     step(j, 0);
-    step(j + 1, 1 % STAGES);
-    if constexpr (STAGES > 2) step(j + 2, 2 % STAGES);
-    if constexpr (STAGES > 3) step(j + 3, 3 % STAGES);
+    step(j + 1, 1);
+    step(j + 2, 2);
   }
 
   // ---- epilogue: O = acc / l (one division per row), LSE = ln 2 * (m + log2 l)
@@ -354,7 +384,7 @@ hipError_t launch_out(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.in_fp32) return launch_fwd_f32(p, stream);
   if (p.head_dim == 64)
-    return p.causal ? launch_out<64, true, 4, 2>(p, stream) : launch_out<64, false, 4, 2>(p, stream);
+    return p.causal ? launch_out<64, true, 4, 3>(p, stream) : launch_out<64, false, 4, 3>(p, stream);
   return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream)
                   : launch_out<128, false, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream);
 }

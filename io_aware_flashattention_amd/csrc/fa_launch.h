@@ -27,11 +27,12 @@ struct DecodeParams {
   const int32_t* seqlens;
   void* o;             // [B, Hq, d]
   float* lse;          // [B, Hq] or null
-  float* part_o;       // workspace [B, Hq, max_splits, d]
-  float* part_lse;     // workspace [B, Hq, max_splits]
+  float* part_o;       // workspace [B*Hkv + n_waves][G][d]
+  float* part_lse;     // workspace [B*Hkv + n_waves][G]
   int64_t kv_stride[3];
   int batch, heads_q, heads_kv, group, max_seqlen, head_dim;
-  int split_tokens, max_splits;
+  int split_tokens;    // lower bound on the keys per wave range (0: none)
+  int n_waves;         // decode grid (one-wave workgroups)
   float scale_log2;
   bool out_fp32;
 };
@@ -40,7 +41,7 @@ struct DecodeParams {
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);       // dispatches on in_fp32
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
-int decode_default_split();
+int decode_waves();
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -98,7 +98,6 @@ def _dec(**kw):
     (dict(d=64), 2, "head_dim"),
     (dict(Hq=16, Hkv=3), 2, "multiple"),
     (dict(Hq=66, Hkv=1), 2, "at most 32"),
-    (dict(split=100), 2, "multiple of 64"),
     (dict(k=FAKE + 4), 2, "aligned"),
     (dict(kvs=(2 * 4096 * 128, 4096 * 128, 132)), 2, "multiples"),
     (dict(wsb=1000), 3, "workspace"),
@@ -112,11 +111,13 @@ def test_decode_rejects_before_launch(kw, status, needle):
 
 def test_decode_workspace_size():
     lib = _lib.load()
-    # 64 sequences x 64 heads x ceil(32768 / 1024) splits x (128 + 1) floats
-    assert lib.fa_decode_workspace_bytes(64, 64, 32768, 128, 1024) == 64 * 64 * 32 * 129 * 4
-    assert lib.fa_decode_workspace_bytes(1, 1, 100, 128, 64) == 2 * 129 * 4
-    assert lib.fa_decode_workspace_bytes(0, 1, 100, 128, 64) == 0
-    assert lib.fa_decode_workspace_bytes(2, 8, 1000, 128, 0) > 0
+    waves = lib.fa_decode_workspace_bytes(1, 1, 1, 100, 128) // (129 * 4) - 1   # decode grid size
+    assert waves > 0
+    # (batch * heads_kv + waves) pieces, each heads_q / heads_kv heads of (128 + 1) floats
+    assert lib.fa_decode_workspace_bytes(64, 64, 8, 32768, 128) == (64 * 8 + waves) * 8 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(2, 8, 8, 1000, 128) == (16 + waves) * 129 * 4
+    assert lib.fa_decode_workspace_bytes(0, 1, 1, 100, 128) == 0
+    assert lib.fa_decode_workspace_bytes(1, 6, 4, 100, 128) == 0
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
