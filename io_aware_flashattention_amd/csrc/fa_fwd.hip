@@ -41,7 +41,25 @@
 #define FA_FWD_NW128 8       // waves per workgroup at head_dim 128
 #endif
 #ifndef FA_FWD_STAGES128
-#define FA_FWD_STAGES128 3   // K/V tiles in flight at head_dim 128
+#define FA_FWD_STAGES128 3   // K/V tiles resident or in flight at head_dim 128
+#endif
+#ifndef FA_FWD_PP128
+#define FA_FWD_PP128 1       // ping-pong kernel for causal head_dim 128
+#endif
+#ifndef FA_FWD_PPST
+#define FA_FWD_PPST 3        // its K/V ring depth
+#endif
+#ifndef FA_FWD_GRP
+#define FA_FWD_GRP 2         // how waves split into the two ping-pong groups
+#endif
+#ifndef FA_FWD_PRIO
+#define FA_FWD_PRIO 0        // raise wave priority during matrix-core units
+#endif
+#ifndef FA_FWD_AHEAD
+#define FA_FWD_AHEAD 4       // fragment-read steps issued ahead of their MFMA
+#endif
+#ifndef FA_FWD_R128
+#define FA_FWD_R128 1        // 32-row blocks per wave at head_dim 128
 #endif
 
 namespace fa {
@@ -71,6 +89,14 @@ template <int D> __device__ __forceinline__ int vswz_t(int r) {
 // compiler needs the address space spelled out).
 typedef __attribute__((address_space(3))) void lds_void;
 
+// max(a, b, c) in one instruction (the compiler splits a chain of fmaxf into
+// two-input and three-input maxima).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -82,9 +108,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 namespace detail {
 
-template <int D, bool CAUSAL, typename TOut, int NW, int STAGES>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdParams p) {
-  constexpr int BRW = 32 * NW;               // query rows per workgroup
+template <int D, bool CAUSAL, typename TOut, int NW, int R, int STAGES>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(R == 1 ? 2 : 1, R == 1 ? 2 : 1)))
+void fwd_bf16_kernel(const FwdParams p) {
+  constexpr int BRW = 32 * R * NW;           // query rows per workgroup (R 32-row blocks per wave)
   constexpr int KSTEPS = D / 16;             // k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
   constexpr int TILE = BC * D;               // bf16 elements per K or V tile
@@ -92,7 +119,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
   constexpr int NLD = TILE * 2 / 1024;       // 1-KB DMA writes per operand tile
   constexpr int LPW = NLD / NW;              // of those, per wave
   static_assert(NLD % NW == 0, "tile / wave mismatch");
-  static_assert(STAGES == 3, "the software pipeline keeps tiles j, j+1 and j+2 in LDS");
+  static_assert(STAGES == 3 || STAGES == 4, "the pipeline keeps tiles j and j+1 resident and loads ahead");
 
   __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE];   // [stage][K, V][TILE]
 
@@ -124,8 +151,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
   const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
 
   const int q0 = qt * BRW;
-  const int wrow0 = q0 + wave * 32;
-  const int row = wrow0 + r32;
+  const int wrow0 = q0 + wave * 32 * R;      // first row of this wave; block rb starts at wrow0 + 32 rb
   const int nq = p.seqlen_q, nk = p.seqlen_k;
   const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;    // skip bound
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -151,12 +177,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
     }
   };
 
-  // ---- this lane's query row as B-operand fragments (rows past the end are 0)
-  bf16x8 qf[KSTEPS];
+  // ---- this lane's query rows as B-operand fragments (rows past the end are 0)
+  bf16x8 qf[R][KSTEPS];
 #pragma unroll
-  for (int kc = 0; kc < KSTEPS; ++kc)
-    qf[kc] = as_bf16x8(row < nq ? load16(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half)
-                                : u32x4{0, 0, 0, 0});
+  for (int rb = 0; rb < R; ++rb) {
+    const int row = wrow0 + 32 * rb + r32;
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc)
+      qf[rb][kc] = as_bf16x8(row < nq ? load16(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half)
+                                      : u32x4{0, 0, 0, 0});
+  }
 
   // ---- lane-constant LDS offsets (elements) of the fragment reads
   int koff[KSTEPS];
@@ -176,101 +206,124 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
     }
   }
 
-  // ---- running state of this lane's row
+  // ---- running state of this lane's R rows
   const float c2 = p.scale_log2;
-  float m_run = kNegInf;          // base of the exponentials (base-2 units)
-  float l_run = 0.f;              // float32 sum of the weights (for the log-sum-exp)
-  float l_o = 0.f;                // sum of the bf16-rounded weights (normalises O)
-  f32x16 o[DBLK];
+  float m_run[R], l_run[R], l_o[R];   // base (base-2 units), float32 sum (LSE), bf16 sum (normalises O)
+  f32x16 o[R][DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+  for (int rb = 0; rb < R; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+    l_o[rb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) o[rb][i] = f32x16{};
+  }
 
   // tiles this wave needs (under the causal mask, the rest lie in its future)
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : ntiles;
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 32 * R - 1) / BC + 1) : ntiles;
 
-  // S^T of one 64-key tile (K in stage ST): two 32-key blocks, chains interleaved
-  auto scores = [&](int ST, f32x16& a0, f32x16& a1) {
+  // S^T of one 64-key tile (K in stage ST) for the R row blocks: each K
+  // fragment read once, used R times
+  auto scores = [&](int ST, f32x16 (&a)[R][2]) {
     const __bf16* ks = smem + ST * 2 * TILE;
-    a0 = f32x16{};
-    a1 = f32x16{};
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) a[rb][0] = a[rb][1] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KSTEPS; ++kc) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
-      a0 = mfma32(k0, qf[kc], a0);
-      a1 = mfma32(k1, qf[kc], a1);
-    }
-  };
-
-  // diagonal / ragged tiles: -inf where the key is in the row's future or past the end
-  auto mask = [&](int kv0, f32x16& a0, f32x16& a1) {
-    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
-        a0[jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : a0[jj];
-        a1[jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : a1[jj];
+      for (int rb = 0; rb < R; ++rb) {
+        a[rb][0] = mfma32(k0, qf[rb][kc], a[rb][0]);
+        a[rb][1] = mfma32(k1, qf[rb][kc], a[rb][1]);
       }
     }
   };
 
-  // row maximum of a tile; moves the base (rescaling O and the sums) only when
-  // some row's maximum grows by more than the threshold (wave-uniform, rare)
-  auto row_max = [&](const f32x16& a0, const f32x16& a1) {
-    float mx = fmaxf(a0[0], a1[0]);          // three-input max chain (v_max3_f32)
+  // diagonal / ragged tiles: -inf where the key is in the row's future or past the end
+  auto mask = [&](int kv0, f32x16 (&a)[R][2]) {
+    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
 #pragma unroll
-    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(a0[jj], a1[jj]));
-    return half_swap_max(mx) * c2;
+      for (int rb = 0; rb < R; ++rb) {
+        const int row = wrow0 + 32 * rb + r32;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
+          a[rb][0][jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : a[rb][0][jj];
+          a[rb][1][jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : a[rb][1][jj];
+        }
+      }
+    }
   };
-  auto move_base = [&](float mt) {
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-      l_run *= alpha;
-      l_o *= alpha;
+
+  // row maxima of a tile; the base moves (rescaling O and the sums) only when
+  // some row's maximum grows by more than the threshold (wave-uniform, rare)
+  auto move_base = [&](const f32x16 (&a)[R][2]) {
+    float mt[R];
+    bool grow = false;
 #pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
-      m_run = m_new;
+    for (int rb = 0; rb < R; ++rb) {
+      float mx = fmaxf(a[rb][0][0], a[rb][1][0]);        // three-input max chain (v_max3_f32)
+#pragma unroll
+      for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, fmaxf(a[rb][0][jj], a[rb][1][jj]));
+      mt[rb] = half_swap_max(mx) * c2;
+      grow = grow || (mt[rb] > m_run[rb] + kRescaleThreshold);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        const float m_new = fmaxf(m_run[rb], mt[rb]);
+        const float alpha = fast_exp2(m_run[rb] - (m_new == kNegInf ? 0.f : m_new));
+        l_run[rb] *= alpha;
+        l_o[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) o[rb][i] *= alpha;
+        m_run[rb] = m_new;
+      }
     }
   };
 
   // weights of a tile against the current base: float32 and bf16 row sums,
   // bf16 P^T chunks of 16 keys as B operands
-  auto weights = [&](f32x16& a0, f32x16& a1, bf16x8 (&pb)[4]) {
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float rs = 0.f;
+  auto weights = [&](f32x16 (&a)[R][2], bf16x8 (&pb)[R][4]) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const float p0 = fast_exp2(fmaf(a0[jj], c2, -m_use));
-      const float p1 = fast_exp2(fmaf(a1[jj], c2, -m_use));
-      a0[jj] = p0;
-      a1[jj] = p1;
-      rs += p0 + p1;
-    }
+    for (int rb = 0; rb < R; ++rb) {
+      const float m_use = m_run[rb] == kNegInf ? 0.f : m_run[rb];
+      float rs = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pb[0][e] = (__bf16)a0[e];
-      pb[1][e] = (__bf16)a0[8 + e];
-      pb[2][e] = (__bf16)a1[e];
-      pb[3][e] = (__bf16)a1[8 + e];
-    }
-    float ro = 0.f;
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16x2 pr;
-        pr[0] = pb[c][2 * e];
-        pr[1] = pb[c][2 * e + 1];
-        ro = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ro, false);
+      for (int jj = 0; jj < 16; ++jj) {
+        const float p0 = fast_exp2(fmaf(a[rb][0][jj], c2, -m_use));
+        const float p1 = fast_exp2(fmaf(a[rb][1][jj], c2, -m_use));
+        a[rb][0][jj] = p0;
+        a[rb][1][jj] = p1;
+        rs += p0 + p1;
       }
-    l_run += half_swap_sum(rs);
-    l_o += half_swap_sum(ro);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[rb][0][e] = (__bf16)a[rb][0][e];
+        pb[rb][1][e] = (__bf16)a[rb][0][8 + e];
+        pb[rb][2][e] = (__bf16)a[rb][1][e];
+        pb[rb][3][e] = (__bf16)a[rb][1][8 + e];
+      }
+      float ro = 0.f;
+      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16x2 pr;
+          pr[0] = pb[rb][c][2 * e];
+          pr[1] = pb[rb][c][2 * e + 1];
+          ro = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ro, false);
+        }
+      l_run[rb] += half_swap_sum(rs);
+      l_o[rb] += half_swap_sum(ro);
+    }
   };
 
-  // O^T += V^T P^T (V in stage ST); V^T fragments by transposing reads, 4 keys each
-  auto accumulate = [&](int ST, const bf16x8 (&pb)[4]) {
+  // O^T += V^T P^T (V in stage ST); V^T fragments by transposing reads, 4 keys
+  // each, read once and used R times
+  auto accumulate = [&](int ST, const bf16x8 (&pb)[R][4]) {
     const __bf16* vs = smem + ST * 2 * TILE + TILE;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -282,60 +335,445 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = mfma32(a, pb[c], o[db]);
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) o[rb][db] = mfma32(a, pb[rb][c], o[rb][db]);
       }
     }
   };
 
   // Software pipeline over tiles. Iteration j holds tile j (V) and tile j+1
-  // (K) in LDS and loads tile j+2: the scores of tile j+1 go to the matrix
-  // cores while the exponentials of tile j run on the vector ALUs, then
-  // O += V_j P_j overlaps the row maximum of tile j+1.
-  f32x16 c0, c1;                    // scores of tile j (the current tile)
+  // (K) in LDS while later tiles load: the scores of tile j+1 go to the
+  // matrix cores while the exponentials of tile j run on the vector ALUs,
+  // then O += V_j P_j overlaps the row maxima of tile j+1.
+  f32x16 cur[R][2];                 // scores of tile j (the current tile)
   issue(0, 0);
   if (1 < ntiles) issue(1, 1);
-  wait_vmcnt<0>();
+  if (STAGES > 3 && 2 < ntiles) issue(2, 2);
+  if (STAGES > 3 && 2 < ntiles) wait_vmcnt<2 * LPW>();   // tiles 0 and 1 landed, 2 may fly
+  else wait_vmcnt<0>();
   __syncthreads();
   if (0 < nt_w) {
-    scores(0, c0, c1);
-    mask(0, c0, c1);
-    move_base(row_max(c0, c1));
+    scores(0, cur);
+    mask(0, cur);
+    move_base(cur);
   }
 
-  auto step = [&](int j, int SV) {          // SV = j % 3: stage of tile j
+  auto step = [&](int j, int SV) {          // SV = j % STAGES: stage of tile j
     if (j >= ntiles) return;
-    const int SK = (SV + 1) % 3;             // stage of tile j+1
-    if (j > 0) {
-      wait_vmcnt<0>();                       // tile j+1 landed (this wave's share)
-      __syncthreads();                       // ... everyone's; tile j-1's stage is free
+    const int SK = (SV + 1) % STAGES;        // stage of tile j+1
+    if (j > 0) {                             // tile j+1 landed (later tiles may fly)
+      if (STAGES > 3 && j + 2 < ntiles) wait_vmcnt<2 * LPW>();
+      else wait_vmcnt<0>();
+      __syncthreads();                       // ... for every wave; tile j-1's stage is free
     }
-    if (j + 2 < ntiles) issue(j + 2, (SV + 2) % 3);
-    const bool cur = j < nt_w, nxt = j + 1 < nt_w;
-    bf16x8 pb[4];
-    f32x16 n0, n1;
-    if (cur && nxt) {
-      scores(SK, n0, n1);                    // matrix cores ...
-      weights(c0, c1, pb);                   // ... alongside the exponentials
-      mask((j + 1) * BC, n0, n1);
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, (SV + STAGES - 1) % STAGES);
+    const bool act = j < nt_w, nxt = j + 1 < nt_w;
+    bf16x8 pb[R][4];
+    f32x16 nx[R][2];
+    if (act && nxt) {
+      scores(SK, nx);                        // matrix cores ...
+      weights(cur, pb);                      // ... alongside the exponentials
+      mask((j + 1) * BC, nx);
       accumulate(SV, pb);                    // matrix cores ...
-      const float mt = row_max(n0, n1);      // ... alongside the next maximum
-      move_base(mt);
-      c0 = n0;
-      c1 = n1;
-    } else if (cur) {                        // this wave's last tile
-      weights(c0, c1, pb);
+      move_base(nx);                         // ... alongside the next maxima
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        cur[rb][0] = nx[rb][0];
+        cur[rb][1] = nx[rb][1];
+      }
+    } else if (act) {                        // this wave's last tile
+      weights(cur, pb);
       accumulate(SV, pb);
     }
   };
 
-  for (int j = 0; j < ntiles; j += 3) {
+  for (int j = 0; j < ntiles; j += STAGES) {
     step(j, 0);
     step(j + 1, 1);
     step(j + 2, 2);
+    if constexpr (STAGES > 3) step(j + 3, 3);
   }
 
   // ---- epilogue: O = acc / l (one division per row), LSE = ln 2 * (m + log2 l)
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    const int row = wrow0 + 32 * rb + r32;
+    if (row >= nq) continue;
+    const float inv_l = l_o[rb] > 0.f ? 1.f / l_o[rb] : 0.f;
+    TOut* op = reinterpret_cast<TOut*>(p.o) + b * p.o_stride[0] + hq * p.o_stride[1] + (int64_t)row * p.o_stride[2];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * half;
+        const float v0 = o[rb][db][4 * gq + 0] * inv_l, v1 = o[rb][db][4 * gq + 1] * inv_l;
+        const float v2 = o[rb][db][4 * gq + 2] * inv_l, v3 = o[rb][db][4 * gq + 3] * inv_l;
+        if constexpr (sizeof(TOut) == 4) {
+          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+        } else {
+          bf16x4 h;
+          h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
+          *reinterpret_cast<bf16x4*>(op + d) = h;
+        }
+      }
+    if (p.lse != nullptr && half == 0) {
+      const float lse = l_run[rb] > 0.f ? (m_run[rb] + __log2f(l_run[rb])) * kLn2 : kNegInf;
+      p.lse[((int64_t)b * p.heads_q + hq) * nq + row] = lse;
+    }
+  }
+}
+
+
+// Ping-pong variant for head_dim 128: eight waves in two groups of four (one
+// wave of each group per SIMD). A wave's work is a chain of units separated by
+// workgroup barriers:
+//   G(j): S_{j+1}^T = K_{j+1} Q^T and O^T += V_j^T P_j^T (matrix cores),
+//   S(j): mask, row maxima, exponentials and row sums of tile j (vector ALUs),
+// in the order G(-1) S(0) G(0) S(1) G(1) ... . Group 1 runs one unit behind
+// group 0, so in every phase between two barriers one wave of each SIMD feeds
+// the matrix core while the other runs the softmax, and the two swap at the
+// next barrier. The K/V ring holds STAGES tiles: tile t is read in phases
+// 2t .. 2t+3 and its stage is refilled with tile t+STAGES at phase 2t+4.
+template <int D, bool CAUSAL, typename TOut, int STAGES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(const FwdParams p) {
+  constexpr int NW = 8;
+  constexpr int BRW = 32 * NW;               // query rows per workgroup
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int TILE = BC * D;
+  constexpr int ROWB = 2 * D;
+  constexpr int NLD = TILE * 2 / 1024;
+  constexpr int LPW = NLD / NW;
+  static_assert(NLD % NW == 0, "tile / wave mismatch");
+  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE];   // [stage][K, V][TILE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int r32 = lane & 31;
+#if FA_FWD_GRP == 0
+  const int grp = wave >> 2;
+#elif FA_FWD_GRP == 1
+  const int grp = wave & 1;
+#else
+  // the two waves that share a SIMD take different groups: each wave reads
+  // its SIMD number and takes a ticket from that SIMD's LDS counter
+  __shared__ int simd_ticket[4];
+  if (tid < 4) simd_ticket[tid] = 0;
+  __syncthreads();
+  int grp;
+  {
+    const int simd = (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;   // HW_ID bits 5:4
+    int tk = 0;
+    if (lane == 0) tk = atomicAdd(&simd_ticket[simd], 1);
+    grp = __builtin_amdgcn_readfirstlane(tk) & 1;
+  }
+#endif
+
+  const int n = gridDim.x;
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, slot = wg >> 3;
+  const int per = n >> 3, rem = n & 7;
+  int L = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int g = L % p.group;
+  L /= p.group;
+  const int t = L % p.n_qtiles;
+  L /= p.n_qtiles;
+  const int kvh = L % p.heads_kv;
+  const int b = L / p.heads_kv;
+  const int hq = kvh * p.group + g;
+  const int qt = CAUSAL ? p.n_qtiles - 1 - t : t;
+
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_stride[0] + hq * p.q_stride[1];
+  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + b * p.k_stride[0] + kvh * p.k_stride[1];
+  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_stride[0] + kvh * p.v_stride[1];
+  const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
+
+  const int q0 = qt * BRW;
+  const int wrow0 = q0 + wave * 32;
+  const int row = wrow0 + r32;
+  const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : ntiles;
+
+  // DMA plan: this lane's 16-byte chunk of each 1-KB write, as a byte offset
+  // inside one key tile, so a load is a scalar tile base plus a 32-bit offset
+  int dma_row[LPW], dma_k[LPW], dma_v[LPW];
+  uint32_t kofs[LPW], vofs[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (wave * LPW + i) * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    dma_row[i] = r;
+    dma_k[i] = 8 * (pc ^ kswz_t<D>(r));
+    dma_v[i] = 8 * (pc ^ vswz_t<D>(r));
+    kofs[i] = (uint32_t)(2 * (r * ks2 + dma_k[i]));
+    vofs[i] = (uint32_t)(2 * (r * vs2 + dma_v[i]));
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int tile, int ST) {
+    const int kv0 = tile * BC;
+    const char* kb = reinterpret_cast<const char*>(kp + (int64_t)kv0 * ks2);
+    const char* vb = reinterpret_cast<const char*>(vp + (int64_t)kv0 * vs2);
+    __bf16* dst = smem + ST * 2 * TILE + wave_u * LPW * 512;
+    if (kv0 + BC <= nk) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(kb + kofs[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + vofs[i]), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
+      }
+    } else {                                   // ragged last tile: rows past the end repeat the last row
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = min(dma_row[i], nk - 1 - kv0);
+        const uint32_t ko = (uint32_t)(2 * (r * ks2 + dma_k[i])), vo = (uint32_t)(2 * (r * vs2 + dma_v[i]));
+        __builtin_amdgcn_global_load_lds((const void*)(kb + ko), (lds_void*)(dst + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + vo), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
+      }
+    }
+  };
+  // wait until at most `ahead` tiles of this wave's loads are still in flight
+  auto wait_tiles = [&](int ahead) {
+    if (ahead <= 0) wait_vmcnt<0>();
+    else if (ahead == 1) wait_vmcnt<2 * LPW>();
+    else wait_vmcnt<4 * LPW>();
+  };
+  // workgroup barrier without the fence of __syncthreads (which would also
+  // drain the loads still in flight for later tiles)
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int kc = 0; kc < KSTEPS; ++kc)
+    qf[kc] = as_bf16x8(row < nq ? load16(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half)
+                                : u32x4{0, 0, 0, 0});
+
+  int koff[KSTEPS];
+  {
+    const int r = sigma32(r32);
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz_t<D>(r));
+  }
+  int voff[DBLK];
+  {
+    const int gg = lane >> 4, i = lane & 15;
+    const int r = 8 * (gg >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
+      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_t<D>(r)) + (col & 7);
+    }
+  }
+
+  const float c2 = p.scale_log2;
+  float m_run = kNegInf, l_run = 0.f;
+  // Sum of the bf16 weights that enter P V, on the matrix core (v_dot2c runs
+  // on the matrix pipe too, so it would stall the other group's MFMAs): a
+  // P^T chunk read as the B operand of v_mfma_f32_16x16x32_bf16 holds, in
+  // column n, keys 0-7 and 8-15 of rows n and n+16; the A operand below is 1
+  // where the key group belongs to the row this lane's accumulator holds
+  // (row lane % 32), so every register of lsum is that row's running sum.
+  f32x4 lsum = f32x4{};
+  bf16x8 lsel;
+  {
+    const __bf16 one = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.f : (__bf16)0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lsel[e] = one;
+  }
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+  f32x16 sc[2];          // scores of the tile the next S unit works on
+  bf16x8 pb[4];          // P^T of the tile the next G unit accumulates
+
+  auto scores = [&](int ST) {
+    const __bf16* ks = smem + ST * 2 * TILE;
+    sc[0] = sc[1] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
+      sc[0] = mfma32(k0, qf[kc], sc[0]);
+      sc[1] = mfma32(k1, qf[kc], sc[1]);
+    }
+  };
+  auto accumulate = [&](int ST) {
+    const __bf16* vs = smem + ST * 2 * TILE + TILE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const __bf16* va = vs + voff[db] + 16 * c * D;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(va));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
+        o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[c], o[db]);
+      }
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[c], lsum, 0, 0, 0);
+    }
+  };
+  // Both halves of a G unit with the LDS fragment reads issued AHEAD steps
+  // before the MFMA that consumes them (a scheduling barrier after each step
+  // keeps that order): K for the 8 score k-steps, then V (two transposing
+  // reads per PV MFMA) for the 16 PV MFMAs.
+  auto gunit = [&](int SK, int SV) {
+    constexpr int AHEAD = FA_FWD_AHEAD;
+    const __bf16* ks = smem + SK * 2 * TILE;
+    const __bf16* vs = smem + SV * 2 * TILE + TILE;
+    bf16x8 kf[KSTEPS][2];
+    bf16x4 vf[4 * DBLK][2];
+    auto read_k = [&](int kc) {
+      kf[kc][0] = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
+      kf[kc][1] = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
+    };
+    auto read_v = [&](int i) {                 // PV step i: key chunk i / DBLK, d block i % DBLK
+      const __bf16* va = vs + voff[i % DBLK] + 16 * (i / DBLK) * D;
+      vf[i][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
+      vf[i][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
+    };
+    // reads in consumption order: K k-steps 0..KSTEPS-1, then V steps 0..4*DBLK-1
+    auto read = [&](int x) {
+      if (x < KSTEPS) read_k(x);
+      else if (x < KSTEPS + 4 * DBLK) read_v(x - KSTEPS);
+    };
+#pragma unroll
+    for (int x = 0; x < AHEAD; ++x) read(x);
+    sc[0] = sc[1] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KSTEPS; ++kc) {
+      __builtin_amdgcn_sched_barrier(0);
+      read(kc + AHEAD);
+      sc[0] = mfma32(kf[kc][0], qf[kc], sc[0]);
+      sc[1] = mfma32(kf[kc][1], qf[kc], sc[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DBLK; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      read(KSTEPS + i + AHEAD);
+      o[i % DBLK] = mfma32(__builtin_shufflevector(vf[i][0], vf[i][1], 0, 1, 2, 3, 4, 5, 6, 7), pb[i / DBLK],
+                           o[i % DBLK]);
+      if (i % DBLK == DBLK - 1)
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[i / DBLK], lsum, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto softmax = [&](int kv0) {
+    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
+        sc[0][jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : sc[0][jj];
+        sc[1][jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : sc[1][jj];
+      }
+    }
+    float mx = max3f(sc[0][0], sc[1][0], sc[0][1]);
+    mx = fmaxf(mx, sc[1][1]);
+#pragma unroll
+    for (int jj = 2; jj < 16; ++jj) mx = max3f(mx, sc[0][jj], sc[1][jj]);
+    const float mt = half_swap_max(mx) * c2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const float p0 = fast_exp2(fmaf(sc[0][jj], c2, -m_use));
+      const float p1 = fast_exp2(fmaf(sc[1][jj], c2, -m_use));
+      sc[0][jj] = p0;
+      sc[1][jj] = p1;
+      rs += p0 + p1;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[0][e] = (__bf16)sc[0][e];
+      pb[1][e] = (__bf16)sc[0][8 + e];
+      pb[2][e] = (__bf16)sc[1][e];
+      pb[3][e] = (__bf16)sc[1][8 + e];
+    }
+    l_run += half_swap_sum(rs);
+  };
+
+  // phase bookkeeping shared by every wave: at the start of phase 2t+4 the
+  // stage of tile t is refilled with tile t+STAGES; before the barrier that
+  // opens phase 2t, tile t must have landed.
+  const int nunits = 2 * ntiles + 1;              // G(-1), S(0), G(0), ..., S(nt-1), G(nt-1)
+  const int nph = nunits + 1;
+  auto phase_begin = [&](int ph) {
+    if (ph >= 4 && !(ph & 1)) {
+      const int tt = (ph - 4) >> 1;
+      if (tt + STAGES < ntiles) issue(tt + STAGES, tt % STAGES);
+    }
+  };
+  auto phase_end = [&](int ph) {
+    if (ph + 1 >= nph) return;
+    if (ph & 1) {
+      const int tt = (ph + 1) >> 1;
+      if (tt < ntiles) wait_tiles(min(ntiles - 1, max(STAGES - 1, tt + STAGES - 3)) - tt);
+    }
+    barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < STAGES; ++i)
+    if (i < ntiles) issue(i, i);
+  wait_tiles(min(STAGES, ntiles) - 1);
+  barrier();
+
+  if (grp == 1) {                                   // group 1 idles through phase 0
+    phase_begin(0);
+    phase_end(0);
+  }
+  // units u = 0 .. 2 ntiles, unrolled over 2 STAGES units so stages are constants
+  for (int u0 = 0; u0 < nunits; u0 += 2 * STAGES) {
+#pragma unroll
+    for (int r = 0; r < 2 * STAGES; ++r) {
+      const int u = u0 + r;
+      if (u >= nunits) break;
+      const int ph = u + grp;
+      phase_begin(ph);
+      if (r & 1) {                                  // S(j), j = (u - 1) / 2
+        const int j = (u - 1) >> 1;
+        if (j < nt_w) softmax(j * BC);
+      } else {                                      // G(j), j = u / 2 - 1
+        const int j = (u >> 1) - 1;
+        const int SK = (r / 2) % STAGES;            // stage of tile j + 1 (a constant once unrolled)
+        const int SV = (r / 2 + STAGES - 1) % STAGES;       // stage of tile j
+#if FA_FWD_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
+        if (j >= 0 && j + 1 < nt_w) gunit(SK, SV);
+        else {
+          if (j + 1 < nt_w) scores(SK);
+          if (j >= 0 && j < nt_w) accumulate(SV);
+        }
+#if FA_FWD_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
+      }
+      phase_end(ph);
+    }
+  }
+  if (grp == 0) phase_begin(nph - 1);              // group 0 idles through the last phase
+
   if (row < nq) {
+    const float l_o = lsum[0];
     const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
     TOut* op = reinterpret_cast<TOut*>(p.o) + b * p.o_stride[0] + hq * p.o_stride[1] + (int64_t)row * p.o_stride[2];
 #pragma unroll
@@ -364,19 +802,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const FwdPara
 
 namespace {
 
-template <int D, bool CAUSAL, typename TOut, int NW, int STAGES>
+template <int D, bool CAUSAL, typename TOut, int NW, int R, int STAGES>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  constexpr int BRW = 32 * R * NW;
   FwdParams q = p;
-  q.n_qtiles = (p.seqlen_q + 32 * NW - 1) / (32 * NW);
+  q.n_qtiles = (p.seqlen_q + BRW - 1) / BRW;
   const int64_t wgs = (int64_t)q.batch * q.heads_q * q.n_qtiles;
-  hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, STAGES>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, q);
+  hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, R, STAGES>), dim3((unsigned)wgs), dim3(NW * 64),
+                     0, stream, q);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int NW, int STAGES>
+template <int D, bool CAUSAL, typename TOut, int STAGES>
+hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
+  FwdParams q = p;
+  q.n_qtiles = (p.seqlen_q + 255) / 256;
+  const int64_t wgs = (int64_t)q.batch * q.heads_q * q.n_qtiles;
+  hipLaunchKernelGGL((detail::fwd_pp_kernel<D, CAUSAL, TOut, STAGES>), dim3((unsigned)wgs), dim3(512), 0, stream, q);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, int NW, int R, int STAGES>
 hipError_t launch_out(const FwdParams& p, hipStream_t stream) {
-  return p.out_fp32 ? launch<D, CAUSAL, float, NW, STAGES>(p, stream)
-                    : launch<D, CAUSAL, __bf16, NW, STAGES>(p, stream);
+  return p.out_fp32 ? launch<D, CAUSAL, float, NW, R, STAGES>(p, stream)
+                    : launch<D, CAUSAL, __bf16, NW, R, STAGES>(p, stream);
 }
 
 }  // namespace
@@ -384,9 +833,13 @@ hipError_t launch_out(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.in_fp32) return launch_fwd_f32(p, stream);
   if (p.head_dim == 64)
-    return p.causal ? launch_out<64, true, 4, 3>(p, stream) : launch_out<64, false, 4, 3>(p, stream);
-  return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream)
-                  : launch_out<128, false, FA_FWD_NW128, FA_FWD_STAGES128>(p, stream);
+    return p.causal ? launch_out<64, true, 4, 1, 3>(p, stream) : launch_out<64, false, 4, 1, 3>(p, stream);
+#if FA_FWD_PP128
+  if (p.causal) return p.out_fp32 ? launch_pp<128, true, float, FA_FWD_PPST>(p, stream)
+                                  : launch_pp<128, true, __bf16, FA_FWD_PPST>(p, stream);
+#endif
+  return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream)
+                  : launch_out<128, false, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream);
 }
 
 }  // namespace fa
