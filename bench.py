@@ -30,6 +30,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -271,8 +272,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_
     copy_write = max((max(vs) for n, vs in write.items() if is_copy(n)), default=None)
     sf = COPY_BYTES / copy_fetch if copy_fetch else 1.0
     sw = COPY_BYTES / copy_write if copy_write else 1.0
-    pre_f = pick(fetch, lambda n: "fwd_kernel" in n)
-    pre_w = pick(write, lambda n: "fwd_kernel" in n)
+    is_fwd = lambda n: re.search(r"fwd_\w*kernel", n) is not None
+    pre_f = pick(fetch, is_fwd)
+    pre_w = pick(write, is_fwd)
     dec_f = (pick(fetch, lambda n: "decode_split" in n) or 0) + (pick(fetch, lambda n: "decode_merge" in n) or 0)
     dec_w = (pick(write, lambda n: "decode_split" in n) or 0) + (pick(write, lambda n: "decode_merge" in n) or 0)
     d = {

@@ -87,8 +87,10 @@ typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 } fa_mask_t;
  * softmax_scale  multiplies Q K^T before the softmax (typically 1/sqrt(head_dim)).
  *
  * Supported: head_dim 64 or 128; heads_q % heads_kv == 0; every pointer 16-byte
- * aligned; every stride a multiple of 8 elements (bf16) or 4 elements (fp32).
- * Otherwise FA_ERR_UNSUPPORTED. q, k, v must not overlap o or lse.
+ * aligned; every stride a multiple of 8 elements (bf16) or 4 elements (fp32);
+ * the row strides k_stride[2] and v_stride[2] at most 2^24 elements (a key
+ * tile is addressed with 32-bit offsets). Otherwise FA_ERR_UNSUPPORTED. q, k, v
+ * must not overlap o or lse.
  */
 FA_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int32_t batch, int32_t heads_q, int32_t heads_kv,

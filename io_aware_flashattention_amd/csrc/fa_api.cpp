@@ -102,6 +102,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     if (o_stride[i] % out_vec)
       return fail(FA_ERR_UNSUPPORTED, "fa_fwd: o strides must be multiples of %d elements", out_vec);
   }
+  if (k_stride[2] > (int64_t(1) << 24) || v_stride[2] > (int64_t(1) << 24))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: k/v row strides above 2^24 elements are not supported");
   const int64_t in_b = in_dtype == FA_DTYPE_BF16 ? 2 : 4, out_b = out_dtype == FA_DTYPE_BF16 ? 2 : 4;
   uintptr_t o0, o1, a0, a1;
   span(o, o_stride, batch, heads_q, seqlen_q, head_dim, out_b, &o0, &o1);

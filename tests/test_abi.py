@@ -71,6 +71,7 @@ def _fwd(**kw):
     (dict(qs=(16384, 8192, 132)), 2, "multiples"),
     (dict(ind=1, qs=(16384, 8192, 130)), 2, "multiples"),
     (dict(o=FAKE + 0x100), 1, "overlaps"),
+    (dict(ks=(8192, 8192, (1 << 24) + 8)), 2, "row strides"),
 ])
 def test_fwd_rejects_before_launch(kw, status, needle):
     st, msg = _fwd(**kw)
