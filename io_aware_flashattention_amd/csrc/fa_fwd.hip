@@ -44,7 +44,7 @@
 #define FA_FWD_STAGES128 3   // K/V tiles resident or in flight at head_dim 128
 #endif
 #ifndef FA_FWD_PP128
-#define FA_FWD_PP128 1       // ping-pong kernel for causal head_dim 128
+#define FA_FWD_PP128 1       // ping-pong kernel for head_dim 128
 #endif
 #ifndef FA_FWD_PPST
 #define FA_FWD_PPST 3        // its K/V ring depth
@@ -88,14 +88,6 @@ template <int D> __device__ __forceinline__ int vswz_t(int r) {
 // LDS pointer type for the direct global -> LDS loads (the host pass of the
 // compiler needs the address space spelled out).
 typedef __attribute__((address_space(3))) void lds_void;
-
-// max(a, b, c) in one instruction (the compiler splits a chain of fmaxf into
-// two-input and three-input maxima).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
 template <int N>
@@ -499,7 +491,11 @@ void fwd_pp_kernel(const FwdParams p) {
   const int nq = p.seqlen_q, nk = p.seqlen_k;
   const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;
   const int ntiles = (kv_end + BC - 1) / BC;
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : ntiles;
+  // Tiles this wave needs. Without the mask that is every tile, but the bound
+  // is still written in terms of the wave's rows (equal to ntiles since
+  // wrow0 >= 0): a wave-uniform bound lets the compiler turn the unit loop
+  // into uniform branches whose register allocation spills.
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : min(ntiles, (wrow0 + nk + BC - 1) / BC);
 
   // DMA plan: this lane's 16-byte chunk of each 1-KB write, as a byte offset
   // inside one key tile, so a load is a scalar tile base plus a 32-bit offset
@@ -576,6 +572,7 @@ void fwd_pp_kernel(const FwdParams p) {
 
   const float c2 = p.scale_log2;
   float m_run = kNegInf, l_run = 0.f;
+  float m_use = 0.f;                    // m_run, or 0 while no key has been seen
   // Sum of the bf16 weights that enter P V, on the matrix core (v_dot2c runs
   // on the matrix pipe too, so it would stall the other group's MFMAs): a
   // P^T chunk read as the B operand of v_mfma_f32_16x16x32_bf16 holds, in
@@ -676,11 +673,20 @@ void fwd_pp_kernel(const FwdParams p) {
         sc[1][jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : sc[1][jj];
       }
     }
-    float mx = max3f(sc[0][0], sc[1][0], sc[0][1]);
-    mx = fmaxf(mx, sc[1][1]);
+    // A single wave issues an independent VALU op about every 5 cycles but a
+    // dependent one only every 10, so the row maximum and the row sum run as
+    // four interleaved chains rather than one.
+    float mq[4];
 #pragma unroll
-    for (int jj = 2; jj < 16; ++jj) mx = max3f(mx, sc[0][jj], sc[1][jj]);
-    const float mt = half_swap_max(mx) * c2;
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& a = sc[c >> 1];
+      const int o8 = 8 * (c & 1);
+      float m = fmaxf(fmaxf(a[o8], a[o8 + 1]), a[o8 + 2]);
+      m = fmaxf(fmaxf(m, a[o8 + 3]), a[o8 + 4]);
+      m = fmaxf(fmaxf(m, a[o8 + 5]), a[o8 + 6]);
+      mq[c] = fmaxf(m, a[o8 + 7]);
+    }
+    const float mt = half_swap_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * c2;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
@@ -689,24 +695,19 @@ void fwd_pp_kernel(const FwdParams p) {
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
       m_run = m_new;
+      m_use = m_new == kNegInf ? 0.f : m_new;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const float p0 = fast_exp2(fmaf(sc[0][jj], c2, -m_use));
-      const float p1 = fast_exp2(fmaf(sc[1][jj], c2, -m_use));
-      sc[0][jj] = p0;
-      sc[1][jj] = p1;
-      rs += p0 + p1;
-    }
+    float rq[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[0][e] = (__bf16)sc[0][e];
-      pb[1][e] = (__bf16)sc[0][8 + e];
-      pb[2][e] = (__bf16)sc[1][e];
-      pb[3][e] = (__bf16)sc[1][8 + e];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {          // P^T chunk c: keys 16c .. 16c+15 of the tile
+        const float pr = fast_exp2(fmaf(sc[c >> 1][8 * (c & 1) + e], c2, -m_use));
+        rq[c] = e == 0 ? pr : rq[c] + pr;
+        pb[c][e] = (__bf16)pr;
+      }
     }
+    const float rs = (rq[0] + rq[1]) + (rq[2] + rq[3]);
     l_run += half_swap_sum(rs);
   };
 
@@ -798,6 +799,7 @@ void fwd_pp_kernel(const FwdParams p) {
   }
 }
 
+
 }  // namespace detail
 
 namespace {
@@ -835,11 +837,15 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.head_dim == 64)
     return p.causal ? launch_out<64, true, 4, 1, 3>(p, stream) : launch_out<64, false, 4, 1, 3>(p, stream);
 #if FA_FWD_PP128
-  if (p.causal) return p.out_fp32 ? launch_pp<128, true, float, FA_FWD_PPST>(p, stream)
-                                  : launch_pp<128, true, __bf16, FA_FWD_PPST>(p, stream);
-#endif
+  if (p.causal)
+    return p.out_fp32 ? launch_pp<128, true, float, FA_FWD_PPST>(p, stream)
+                      : launch_pp<128, true, __bf16, FA_FWD_PPST>(p, stream);
+  return p.out_fp32 ? launch_pp<128, false, float, FA_FWD_PPST>(p, stream)
+                    : launch_pp<128, false, __bf16, FA_FWD_PPST>(p, stream);
+#else
   return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream)
                   : launch_out<128, false, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream);
+#endif
 }
 
 }  // namespace fa
