@@ -7,6 +7,9 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
      kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
      and merge kernel).
+After the timed steps, the same decode is timed again against a paged cache
+(fa_decode_paged: 16-token pages in a token-major pool, shuffled block table)
+and reported as ``decode_paged``; it is not part of the step.
 Inputs are generated and uploaded before the timed region. W untimed warmup
 steps, then exactly K timed steps between two device synchronisations. Kernel
 durations come from HIP events recorded on the stream the kernels run on.
@@ -41,6 +44,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz 
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 PREFILL_CFG = "c4a_gqa_8k"
 DECODE_CFG = "c5_decode"
+PAGE_SIZE = 16                # tokens per page of the paged-decode measurement
 PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.json")
 KERNEL_SOURCES = ["io_aware_flashattention_amd/csrc/fa_fwd.hip", "io_aware_flashattention_amd/csrc/fa_decode.hip",
                   "io_aware_flashattention_amd/csrc/fa_device.h"]
@@ -124,12 +128,37 @@ def run(args):
     step_ms = [e[0].elapsed_time(e[2]) for e in events]
     print(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms wall", file=sys.stderr, flush=True)
 
+    # paged-KV decode of the same workload, timed on its own after the steps
+    print(f"[bench] generating the paged form of {dc.name} (page size {PAGE_SIZE}, token-major)",
+          file=sys.stderr, flush=True)
+    _, pk, pv, ptab, plens = W.make_paged_decode_inputs(dc, PAGE_SIZE, layout="token", pad="zero")
+    assert np.array_equal(plens, lens)
+    pk_d, pv_d = to_dev(pk).transpose(1, 2), to_dev(pv).transpose(1, 2)   # indexed [page, kv head, slot, d]
+    del pk, pv
+    ptab_d = torch.from_numpy(ptab).to(dev)
+
+    def paged():
+        fa.decode_paged(dq_d, pk_d, pv_d, ptab_d, lens_d, scale=dc.scale, out=do, lse=dlse, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        paged()
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        pev[i][0].record(stream)
+        paged()
+        pev[i][1].record(stream)
+    torch.cuda.synchronize()
+    pag_ms = [e[0].elapsed_time(e[1]) for e in pev]
+
     pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
     kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
     pre_avg = sum(pre_ms) / len(pre_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
     pre_tflops = pre_flops / (pre_avg * 1e-3) / 1e12
     dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    pag_avg = sum(pag_ms) / len(pag_ms)
+    pag_gbs = kv_bytes / (pag_avg * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / args.steps
 
     traffic, traffic_dec = load_traffic()
@@ -157,6 +186,10 @@ def run(args):
         "prefill_ms": round(pre_avg, 4),
         "decode_ms": round(dec_avg, 4),
         "decode_value": {"value": round(dec_gbs, 1), "unit": "GB/s", "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "decode_paged": {"ms": round(pag_avg, 4), "value": round(pag_gbs, 1), "unit": "GB/s",
+                         "frac_hbm_peak": round(pag_gbs / PEAK_HBM_GBS, 4), "page_size": PAGE_SIZE,
+                         "pool": "token-major [page, slot, kv head, d], shuffled block table",
+                         "kernel": "fa_decode_paged (split + merge)"},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fa_fwd (causal, d=128, bf16)"},
@@ -275,8 +308,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_
     is_fwd = lambda n: re.search(r"fwd_\w*kernel", n) is not None
     pre_f = pick(fetch, is_fwd)
     pre_w = pick(write, is_fwd)
-    dec_f = (pick(fetch, lambda n: "decode_split" in n) or 0) + (pick(fetch, lambda n: "decode_merge" in n) or 0)
-    dec_w = (pick(write, lambda n: "decode_split" in n) or 0) + (pick(write, lambda n: "decode_merge" in n) or 0)
+    # contiguous decode only: the paged instantiation of the split kernel is told apart by its template flag;
+    # the merge kernel is shared, so its per-launch average covers both
+    is_split = lambda n: "decode_split" in n and "true" not in n
+    dec_f = (pick(fetch, is_split) or 0) + (pick(fetch, lambda n: "decode_merge" in n) or 0)
+    dec_w = (pick(write, is_split) or 0) + (pick(write, lambda n: "decode_merge" in n) or 0)
     d = {
         "kernel_sources": sources_hash(),
         "command_fetch": cmd_fetch, "command_write": cmd_write,
@@ -311,8 +347,8 @@ def main():
         return summarize_pmc(*args.summarize_pmc, args.out, cmds[0], cmds[1])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.exit("bench.py measures one GPU: the attention path here runs on a single MI355X; "
-                 "multi-GPU runs are not part of this build (--gpus 1 only)")
+        sys.exit("bench.py measures one GPU (--gpus 1): the attention path runs on a single MI355X "
+                 "and has no multi-GPU mode")
     run(args)
 
 

@@ -143,6 +143,45 @@ FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_c
                       fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_paged -- fa_decode against a paged KV cache: the cache lives in
+ * fixed-size pages that need not be contiguous or in order, and a block table
+ * maps each sequence's logical blocks of page_size tokens to physical pages
+ * ("FlashAttention Explained: IO-Aware Attention, Tiling, Online Softmax and
+ * FP8 on Hopper", section "Decoding, Paged and Split-KV Variants": a paged
+ * kernel reads keys and values through the block table). Token t of sequence
+ * b is slot t % page_size of page block_table[b * max_blocks_per_seq +
+ * t / page_size]. The split, the arithmetic and the merge are those of
+ * fa_decode, so on the same cached values the two return identical bits.
+ *
+ * q            [batch, heads_q, head_dim] bf16, contiguous
+ * k_pages      num_pages pages of page_size tokens x heads_kv heads, bf16;
+ *              element (page, kv head, slot, d) at
+ *              page * page_stride[0] + head * page_stride[1] + slot * page_stride[2] + d
+ *              (any order of the three outer axes, head_dim contiguous)
+ * v_pages      same layout and strides as k_pages
+ * block_table  DEVICE int32 [batch, max_blocks_per_seq]; only the entries of
+ *              blocks that hold one of the first seqlens_k[b] tokens are read.
+ *              An entry outside [0, num_pages) is clamped into it (the result is
+ *              then meaningless, but no access leaves the page arrays).
+ * seqlens_k    DEVICE int32 [batch], clamped to [0, max_blocks_per_seq * page_size];
+ *              a length of 0 yields O = 0 and LSE = -inf
+ * o, lse, out_dtype, softmax_scale, split_tokens: as for fa_decode
+ * workspace    at least fa_decode_workspace_bytes(batch, heads_q, heads_kv,
+ *              max_blocks_per_seq * page_size, head_dim) bytes, 16-byte aligned
+ *
+ * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
+ * page_size >= 16 (a 32-key block then spans at most three pages); pointers
+ * 16-byte aligned; page strides multiples of 8 elements. Otherwise
+ * FA_ERR_UNSUPPORTED.
+ */
+FA_API fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                            int32_t num_pages, int32_t page_size, int32_t max_blocks_per_seq,
+                            const int64_t page_stride[3], fa_dtype_t out_dtype, float softmax_scale,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. Never NULL. */
 FA_API const char* fa_status_string(fa_status_t status);
 

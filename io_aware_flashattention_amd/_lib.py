@@ -21,7 +21,7 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode", "fa_status_string",
+EXPORTED = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string",
             "fa_last_error_message")
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
@@ -51,6 +51,11 @@ def load():
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
                               ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
+    lib.fa_decode_paged.restype = ctypes.c_int
+    lib.fa_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,      # q, k/v pages, table, seqlens, o, lse
+                                    _i32, _i32, _i32, _i32,                  # batch, heads_q, heads_kv, head_dim
+                                    _i32, _i32, _i32, _i64p,                 # num_pages, page_size, max_blocks, strides
+                                    ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_last_error_message.restype = ctypes.c_char_p
@@ -147,5 +152,49 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
                        B, Hq, Hkv, Lmax, d, _strides3(k_cache), _dtype_code(out.dtype), float(scale),
                        int(split_tokens), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                        _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 seqlens: torch.Tensor, scale: float | None = None, split_tokens: int = 0,
+                 out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | bool | None = True, workspace: torch.Tensor | None = None):
+    """Split-KV decode against a paged cache.
+
+    q [B,Hq,d] bf16; k_pages/v_pages indexed [page, kv head, slot, d] bf16 with
+    any strides on the first three axes (a token-major pool [P, page_size,
+    Hkv, d] is passed as ``pool.transpose(1, 2)``); block_table int32
+    [B, max_blocks]; seqlens int32 [B]; all on the GPU.
+    """
+    lib = load()
+    B, Hq, d = q.shape
+    P, Hkv, ps = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k_pages.stride() != v_pages.stride() or k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages must share shape and strides")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+        raise ValueError("seqlens must be a contiguous int32 tensor of length batch")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = decode_workspace_bytes(B, Hq, Hkv, max_blocks * ps, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                             seqlens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                             B, Hq, Hkv, d, P, ps, max_blocks, _strides3(k_pages), _dtype_code(out.dtype),
+                             float(scale), int(split_tokens), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st)
     return out, lse

@@ -48,6 +48,65 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 extern "C" {
 
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                            int32_t num_pages, int32_t page_size, int32_t max_blocks_per_seq,
+                            const int64_t page_stride[3], fa_dtype_t out_dtype, float softmax_scale,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !o || !page_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_decode_paged: q, pages, block_table, seqlens_k, o and page_stride must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || head_dim <= 0 || num_pages <= 0 || page_size <= 0 ||
+      max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: sizes must be positive");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: softmax_scale must be finite and positive (got %g)",
+                (double)softmax_scale);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: unknown out_dtype %d", (int)out_dtype);
+  for (int i = 0; i < 3; ++i)
+    if (page_stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: strides must be non-negative");
+  if ((int64_t)max_blocks_per_seq * page_size > 0x7fffffffLL - 64)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: max_blocks_per_seq * page_size overflows int32");
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d not supported (128)", head_dim);
+  if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_decode_paged: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head",
+                heads_q, heads_kv);
+  if (page_size < 16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: page_size %d not supported (at least 16)", page_size);
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(workspace))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: q, pages, o and workspace must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (page_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: page strides must be multiples of 8 elements");
+  const int max_seqlen = max_blocks_per_seq * page_size;
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  if ((int64_t)batch * heads_q > 0x7fffffffLL / 4 || (int64_t)batch * max_blocks_per_seq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: problem too large for one launch");
+
+  fa::DecodeParams p{};
+  p.q = q; p.k = k_pages; p.v = v_pages; p.seqlens = seqlens_k; p.o = o; p.lse = lse;
+  const int64_t parts = ((int64_t)batch * heads_kv + fa::decode_waves()) * (heads_q / heads_kv);
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + parts * head_dim;
+  for (int i = 0; i < 3; ++i) p.kv_stride[i] = page_stride[i];
+  p.block_table = block_table;
+  p.page_size = page_size; p.max_blocks = max_blocks_per_seq; p.num_pages = num_pages;
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+  p.max_seqlen = max_seqlen; p.head_dim = head_dim;
+  p.split_tokens = split_tokens > 0 ? split_tokens : 0;
+  p.n_waves = fa::decode_waves();
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  hipError_t e = fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fa_status_string(fa_status_t s) {
   switch (s) {
     case FA_OK: return "FA_OK";

@@ -28,6 +28,14 @@
 //     accumulator rescaled only when a maximum grows by more than 2^8; O is
 //     normalised by the sum of the bf16-rounded weights, the log-sum-exp uses
 //     the float32 sum.
+//
+// Paged cache (same section: keys and values are fetched through a block
+// table). Token t of a sequence sits in slot t % page_size of the page the
+// table names for logical block t / page_size. A 32-key block then touches at
+// most three pages (page_size >= 16): the wave reads their table entries with
+// scalar loads one block ahead of the DMA that needs them, so the lookup never
+// waits on the vector-memory counter the DMA ring is paced by, and each lane
+// picks its row's page and slot with a compare, not a division.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -64,8 +72,13 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ int kswz_d(int r) { return sigma32(r & 31) & 15; }
 __device__ __forceinline__ int vswz_d(int r) { return 4 * (r & 3); }
 
+// Lengths and block-table entries are read at wave-uniform addresses through
+// the constant address space, so they become scalar loads: they wait on the
+// LDS/scalar counter, never on the vector-memory counter that paces the DMA.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
 __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
-  return min(max(p.seqlens[b], 0), p.max_seqlen);
+  return min(max(((const const_i32*)p.seqlens)[b], 0), p.max_seqlen);
 }
 
 // Tokens per wave range, identical in both kernels: at least split_tokens, a
@@ -83,11 +96,20 @@ struct Cursor {
   int64_t slab_off;          // stream offset of the slab's first token
 };
 
+// Pages under one 32-key block of a paged cache: the table entries of the
+// block's first three logical pages (raw, so that the scalar loads stay in
+// flight until the DMA issue needs them), and the block's first and last key
+// as slots counted from the start of the first page.
+struct PageRun {
+  int e0, e1, e2;
+  int off, lim;
+};
+
 }  // namespace
 
 namespace detail {
 
-template <typename TOut>
+template <typename TOut, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -148,20 +170,52 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   // ---- DMA of one block: eight 1-KB writes per operand, rows past the piece clamped
   const int drow = lane >> 4;                  // row of the lane's chunk, + 4 per write
   const int dchunk = lane & 15;
-  auto issue = [&](const Cursor& c, int st) {
-    const int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
-    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + base;
-    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + base;
+  // Paged cache: table entries of the block at cursor c (scalar loads through
+  // the constant address space; ids outside [0, num_pages) are clamped).
+  auto pages_of = [&](const Cursor& c) {
+    PageRun pr{};
+    if constexpr (PAGED) {
+      const int ps = p.page_size;
+      const int pg0 = c.pos / ps;
+      const int pgl = (c.end - 1) / ps;
+      const const_i32* bt = (const const_i32*)p.block_table + (int64_t)c.b * p.max_blocks;
+      pr.e0 = bt[pg0];
+      pr.e1 = bt[min(pg0 + 1, pgl)];
+      pr.e2 = bt[min(pg0 + 2, pgl)];
+      pr.off = c.pos - pg0 * ps;
+      pr.lim = c.end - 1 - pg0 * ps;
+    }
+    return pr;
+  };
+  auto issue = [&](const Cursor& c, int st, const PageRun& pr) {
+    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k);
+    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v);
+    int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
+    int64_t base1 = 0, base2 = 0;
+    if constexpr (PAGED) {
+      const int top = p.num_pages - 1;
+      const int64_t hofs = (int64_t)c.kvh * p.kv_stride[1];
+      base = (int64_t)min(max(pr.e0, 0), top) * p.kv_stride[0] + hofs;
+      base1 = (int64_t)min(max(pr.e1, 0), top) * p.kv_stride[0] + hofs;
+      base2 = (int64_t)min(max(pr.e2, 0), top) * p.kv_stride[0] + hofs;
+    }
     const int last = c.end - 1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + drow;
-      const int key = min(c.pos + r, last);
+      int64_t row;
+      if constexpr (PAGED) {
+        const int ps = p.page_size;
+        const int kr = min(pr.off + r, pr.lim);           // slot counted from the first page
+        const int j = (kr >= ps) + (kr >= 2 * ps);
+        row = (j == 0 ? base : j == 1 ? base1 : base2) + (int64_t)(kr - j * ps) * p.kv_stride[2];
+      } else {
+        row = base + (int64_t)min(c.pos + r, last) * p.kv_stride[2];
+      }
       __bf16* dk = smem + st * 2 * BLK + i * 512;
-      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * p.kv_stride[2] + 8 * (dchunk ^ kswz_d(r))),
-                                       (lds_void*)dk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)key * p.kv_stride[2] + 8 * (dchunk ^ vswz_d(r))),
-                                       (lds_void*)(dk + BLK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kp + row + 8 * (dchunk ^ kswz_d(r))), (lds_void*)dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + row + 8 * (dchunk ^ vswz_d(r))), (lds_void*)(dk + BLK), 16,
+                                       0, 0);
     }
   };
 
@@ -193,20 +247,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
   // prologue: NST-1 blocks in flight
   Cursor dma = cur;
+  PageRun dma_pages = pages_of(dma);
   bool dma_ok = true;
   int issued = 0;
   for (int s = 0; s < NST - 1 && dma_ok; ++s) {
-    issue(dma, s);
+    issue(dma, s, dma_pages);
     ++issued;
     dma_ok = advance(dma);
+    if (dma_ok) dma_pages = pages_of(dma);
   }
 
   for (int blk = 0;; ++blk) {
     const int st = blk % NST;
     if (dma_ok) {                              // refill the stage block blk-1 used
-      issue(dma, (blk + NST - 1) % NST);
+      issue(dma, (blk + NST - 1) % NST, dma_pages);
       ++issued;
       dma_ok = advance(dma);
+      if (dma_ok) dma_pages = pages_of(dma); // table entries for the next issue
     }
     const int ahead = issued - blk - 1;        // blocks allowed to stay in flight
     if (ahead >= 3) wait_vmcnt<48>();
@@ -367,7 +424,10 @@ namespace {
 
 template <typename TOut>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((detail::decode_split_kernel<TOut>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
+  if (p.block_table != nullptr)
+    hipLaunchKernelGGL((detail::decode_split_kernel<TOut, true>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((detail::decode_split_kernel<TOut, false>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.heads_q;

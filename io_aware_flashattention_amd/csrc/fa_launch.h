@@ -29,7 +29,9 @@ struct DecodeParams {
   float* lse;          // [B, Hq] or null
   float* part_o;       // workspace [B*Hkv + n_waves][G][d]
   float* part_lse;     // workspace [B*Hkv + n_waves][G]
-  int64_t kv_stride[3];
+  int64_t kv_stride[3];     // contiguous cache: {b, h, n}; paged cache: {page, h, slot}
+  const int32_t* block_table;   // paged cache only: [batch][max_blocks] page ids (null: contiguous)
+  int page_size, max_blocks, num_pages;
   int batch, heads_q, heads_kv, group, max_seqlen, head_dim;
   int split_tokens;    // lower bound on the keys per wave range (0: none)
   int n_waves;         // decode grid (one-wave workgroups)

@@ -18,7 +18,13 @@ Recipe (the pages give shapes and "drawn from N(0,1)" but no generator):
 * the decode workload draws each sequence's KV length uniformly from
   [1024, 32768] inclusive; cache rows past a sequence's length are filled
   with a pad value (NaN in tests, so over-reads poison the result; zero in
-  the benchmark).
+  the benchmark);
+* the paged form of a decode workload holds the same token values in a pool
+  of fixed-size pages: every sequence gets ceil(L_b / page_size) pages, the
+  pages of all sequences are a random permutation of the pool (stream
+  ``[seed, tag=6]``), one extra pool page is filled with the pad value and
+  every unused block-table entry names it, and slots past L_b in a
+  sequence's last page hold the pad value too.
 """
 from __future__ import annotations
 
@@ -28,7 +34,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TAG_Q, TAG_K, TAG_V, TAG_HEAVY, TAG_LENS = 1, 2, 3, 4, 5
+TAG_Q, TAG_K, TAG_V, TAG_HEAVY, TAG_LENS, TAG_PAGES = 1, 2, 3, 4, 5, 6
 BF16_NAN = np.uint16(0x7FC0)
 
 
@@ -218,6 +224,53 @@ def make_decode_inputs(cfg: DecodeConfig, pad: str = "nan", lengths=None):
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(run, jobs))
     return q, kc, vc, lens
+
+
+def make_paged_decode_inputs(cfg: DecodeConfig, page_size: int, layout: str = "head", pad: str = "nan",
+                             lengths=None):
+    """Paged cache holding the same values as ``make_decode_inputs``.
+
+    Returns q [B,Hq,d], k_pool/v_pool, block_table [B, ceil(max_len/page_size)]
+    int32, lengths [B] int32. layout "head": pools are [P, Hkv, page_size, d];
+    layout "token": [P, page_size, Hkv, d] (vLLM-style). Token t of (b, kv head)
+    is stored in page block_table[b, t // page_size], slot t % page_size.
+    """
+    if layout not in ("head", "token"):
+        raise ValueError(layout)
+    lens = decode_lengths(cfg) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    B, Hkv, d, ps = cfg.batch, cfg.heads_kv, cfg.head_dim, page_size
+    q = np.stack([decode_query(cfg, b) for b in range(B)])
+    nblk = [-(-int(L) // ps) for L in lens]
+    max_blocks = -(-cfg.max_len // ps)
+    n_pages = sum(nblk) + 1
+    rng = np.random.Generator(np.random.PCG64([cfg.seed, TAG_PAGES]))
+    perm = rng.permutation(n_pages).astype(np.int32)
+    poison = int(perm[-1])
+    table = np.full((B, max_blocks), poison, dtype=np.int32)
+    used = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[used:used + nblk[b]]
+        used += nblk[b]
+    padv = BF16_NAN if pad == "nan" else np.uint16(0)
+    shape = (n_pages, Hkv, ps, d) if layout == "head" else (n_pages, ps, Hkv, d)
+    kp = np.full(shape, padv, dtype=np.uint16)
+    vp = np.full(shape, padv, dtype=np.uint16)
+
+    def run(job):
+        w, b, h = job
+        dst = kp if w == "k" else vp
+        L, n = int(lens[b]), nblk[b]
+        rows = np.full((n * ps, d), padv, dtype=np.uint16)
+        rows[:L] = decode_kv_slice(cfg, w, b, h, L)
+        if layout == "head":
+            dst[table[b, :n], h] = rows.reshape(n, ps, d)
+        else:
+            dst[table[b, :n], :, h] = rows.reshape(n, ps, d)
+
+    jobs = [(w, b, h) for w in ("k", "v") for b in range(B) for h in range(Hkv)]
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(run, jobs))
+    return q, kp, vp, table, lens
 
 
 def to_f64(x: np.ndarray) -> np.ndarray:

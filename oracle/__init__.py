@@ -4,7 +4,8 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package. The product path never does.
 """
 from .attention import (attention_ref, block_summary, decode_ref, merge_lse,
-                        merge_summaries, split_decode_ref, stream_attention)
+                        merge_summaries, paged_decode_ref, paged_rows, split_decode_ref,
+                        stream_attention)
 
 __all__ = ["attention_ref", "stream_attention", "block_summary", "merge_summaries",
-           "merge_lse", "decode_ref", "split_decode_ref"]
+           "merge_lse", "decode_ref", "split_decode_ref", "paged_rows", "paged_decode_ref"]

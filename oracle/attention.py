@@ -32,6 +32,12 @@ What it computes, and where the pages define it:
   Split-KV Variants".)
 * ``decode_ref`` -- single-token decode: the same attention for one query row
   per head over the first L_b cached keys of each sequence.
+* ``paged_rows`` / ``paged_decode_ref`` -- the same decode over a paged cache:
+  fixed-size pages addressed through a per-sequence block table, token t of
+  a sequence in slot t mod page_size of the page that the table names for
+  logical block floor(t / page_size). ("FlashAttention Explained" section
+  "Decoding, Paged and Split-KV Variants": the cache lives in non-contiguous
+  fixed-size blocks found through a block table.)
 
 Readings where the pages are silent (each listed in the design notes):
 GQA maps query head h to kv head h // (Hq / Hkv); key c is visible to query
@@ -57,9 +63,10 @@ def _softmax_rows(S: np.ndarray):
     """Safe softmax of each row of S (entries may be -inf).
 
     Returns (P, m, l): P = exp(S - m) / l with m the row max and l the row sum
-    of exp(S - m). Rows whose entries are all -inf get P = 0, m = -inf, l = 0.
+    of exp(S - m). Rows whose entries are all -inf, or that have no entries
+    (no key at all), get P = 0, m = -inf, l = 0.
     """
-    m = S.max(axis=1)
+    m = S.max(axis=1, initial=-np.inf)
     live = np.isfinite(m)
     shift = np.where(live, m, 0.0)
     E = np.exp(S - shift[:, None])          # exp(-inf) = 0 for masked entries
@@ -237,4 +244,38 @@ def split_decode_ref(q, k_cache, v_cache, seqlens, scale: float, split: int, bat
                                    _as64(v_cache[b, :, c0:c1])[None], scale)
             parts.append((ob[0, :, 0], lb[0, :, 0]))
         O[b], L[b] = merge_lse(parts)
+    return O, L
+
+
+def paged_rows(pool, block_table, b: int, n: int):
+    """Rows 0..n-1 of every kv head of sequence b, read through the block table.
+
+    pool is indexed [page, kv head, slot, d] (any strides); returns [Hkv, n, d].
+    Only table entries of blocks that hold one of the n tokens are read.
+    """
+    pool = np.asarray(pool)
+    ps = pool.shape[2]
+    t = np.arange(n)
+    pages = np.asarray(block_table)[b, t // ps]               # [n]
+    return pool[pages, :, t % ps].transpose(1, 0, 2)         # [n, H, d] -> [H, n, d]
+
+
+def paged_decode_ref(q, k_pool, v_pool, block_table, seqlens, scale: float, batches=None, values=None):
+    """decode_ref over a paged cache: q [B, Hq, d]; pools [page, Hkv, slot, d];
+    block_table [B, max_blocks]; seqlens [B]. Returns O [B, Hq, dv], LSE [B, Hq].
+
+    ``values`` maps gathered pool entries to numbers (for pools stored as
+    bfloat16 bit patterns), so that only the rows a sequence uses are widened.
+    """
+    B, Hq, d = np.shape(q)
+    O = np.zeros((B, Hq, np.shape(v_pool)[3]))
+    L = np.full((B, Hq), -np.inf)
+    conv = values if values is not None else (lambda x: x)
+    for b in (range(B) if batches is None else batches):
+        n = int(seqlens[b])
+        kb = _as64(conv(paged_rows(k_pool, block_table, b, n)))
+        vb = _as64(conv(paged_rows(v_pool, block_table, b, n)))
+        ob, lb = attention_ref(_as64(q[b])[None, :, None, :], kb[None], vb[None], scale)
+        O[b] = ob[0, :, 0]
+        L[b] = lb[0, :, 0]
     return O, L

@@ -110,6 +110,41 @@ def test_decode_rejects_before_launch(kw, status, needle):
     assert needle in msg
 
 
+def _paged(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, bt=FAKE + 0x300000, lens=FAKE + 0x380000,
+             o=FAKE + 0x400000, lse=None, B=2, Hq=16, Hkv=2, d=128, P=64, ps=16, mb=32,
+             pst=(2 * 16 * 128, 16 * 128, 128), outd=0, scale=0.0884, split=0, ws=FAKE + 0x800000, wsb=1 << 30)
+    a.update(kw)
+    pst = (ctypes.c_int64 * 3)(*a["pst"]) if a["pst"] is not None else None
+    st = lib.fa_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"],
+                             a["Hkv"], a["d"], a["P"], a["ps"], a["mb"], pst, a["outd"], a["scale"], a["split"],
+                             a["ws"], a["wsb"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(bt=None), 1, "non-null"),
+    (dict(pst=None), 1, "non-null"),
+    (dict(P=0), 1, "positive"),
+    (dict(mb=0), 1, "positive"),
+    (dict(ps=-16), 1, "positive"),
+    (dict(pst=(-4096, 2048, 128)), 1, "non-negative"),
+    (dict(mb=1 << 27, ps=32), 1, "overflows"),
+    (dict(outd=3), 1, "out_dtype"),
+    (dict(d=64), 2, "head_dim"),
+    (dict(Hq=16, Hkv=3), 2, "multiple"),
+    (dict(ps=8), 2, "page_size"),
+    (dict(v=FAKE + 0x200004), 2, "aligned"),
+    (dict(pst=(4096, 2048, 132)), 2, "multiples"),
+    (dict(wsb=100), 3, "workspace"),
+])
+def test_decode_paged_rejects_before_launch(kw, status, needle):
+    st, msg = _paged(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def test_decode_workspace_size():
     lib = _lib.load()
     waves = lib.fa_decode_workspace_bytes(1, 1, 1, 100, 128) // (129 * 4) - 1   # decode grid size

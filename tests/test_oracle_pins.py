@@ -10,7 +10,7 @@ from hypothesis import given, settings
 from hypothesis import strategies as st
 
 from oracle import (attention_ref, block_summary, decode_ref, merge_lse, merge_summaries,
-                    split_decode_ref, stream_attention)
+                    paged_decode_ref, paged_rows, split_decode_ref, stream_attention)
 from tests.conftest import golden
 
 
@@ -341,6 +341,16 @@ def test_decode_ignores_padding_and_matches_prefill_row():
     assert np.abs(O[1] - np.repeat(vc[1, :, 0], Hq // Hkv, axis=0)).max() < 1e-15
 
 
+def test_no_key_gives_zero_output_and_minus_inf_lse():
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 2, 3, 4))
+    O, L = attention_ref(q, np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 0, 5)), 0.5)
+    assert O.shape == (1, 2, 3, 5) and np.all(O == 0) and np.all(np.isneginf(L))
+    kc = rng.standard_normal((2, 1, 6, 4))
+    O, L = decode_ref(q[0, :, 0][None].repeat(2, 0), kc, kc, np.array([0, 6]), 0.5)
+    assert np.all(O[0] == 0) and np.all(np.isneginf(L[0])) and np.all(np.isfinite(L[1]))
+
+
 def test_merge_lse_edge_cases():
     rng = np.random.default_rng(41)
     o = rng.standard_normal((3, 4))
@@ -351,3 +361,81 @@ def test_merge_lse_edge_cases():
     assert np.abs(o2 - o).max() < 1e-15 and np.abs(l2 - lse).max() < 1e-15
     o3, l3 = merge_lse([(o, lse), (o, lse)])
     assert np.abs(o3 - o).max() < 1e-15 and np.abs(l3 - lse - math.log(2)).max() < 1e-14
+
+
+# ------------------------------------------------------------- paged cache --
+
+def test_paged_rows_hand_example():
+    """Page size 4, table [2, 0, 1]: tokens 0-3 live in page 2, 4-7 in page 0,
+    8 in page 1 (slot = token mod 4). Entry values encode page, head and slot."""
+    P, H, ps, d = 3, 2, 4, 1
+    pool = np.zeros((P, H, ps, d))
+    for pg in range(P):
+        for h in range(H):
+            for sl in range(ps):
+                pool[pg, h, sl, 0] = 1000 * pg + 100 * h + sl
+    table = np.array([[2, 0, 1, 77]])          # the last entry is past the 9 tokens: never read
+    rows = paged_rows(pool, table, 0, 9)
+    assert rows.shape == (H, 9, d)
+    assert rows[1, :, 0].tolist() == [2100, 2101, 2102, 2103, 100, 101, 102, 103, 1100]
+    assert rows[0, :, 0].tolist() == [2000, 2001, 2002, 2003, 0, 1, 2, 3, 1000]
+    assert paged_rows(pool, table, 0, 0).shape == (H, 0, d)
+
+
+@pytest.mark.parametrize("ps", [4, 16, 24])
+@pytest.mark.parametrize("token_major", [False, True])
+def test_paged_decode_equals_contiguous(ps, token_major):
+    """A contiguous cache copied page by page into a shuffled pool gives the
+    identical decode result; slots past a length hold NaN and table entries
+    past the last block are out of range, so any stray read fails."""
+    rng = np.random.default_rng(51 + ps)
+    B, Hq, Hkv, d, Lmax = 3, 4, 2, 8, 70
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, Hkv, Lmax, d))
+    vc = rng.standard_normal((B, Hkv, Lmax, d))
+    lens = np.array([70, 1, 33])
+    nblk = [-(-int(n) // ps) for n in lens]
+    P = sum(nblk)
+    order = rng.permutation(P)
+    table = np.full((B, -(-Lmax // ps)), 10 ** 9, dtype=np.int64)
+    kpool = np.full((P, Hkv, ps, d), np.nan)
+    vpool = np.full((P, Hkv, ps, d), np.nan)
+    nxt = 0
+    for b in range(B):
+        for j in range(nblk[b]):
+            pg = order[nxt]
+            nxt += 1
+            table[b, j] = pg
+            for sl in range(ps):
+                t = j * ps + sl
+                if t < lens[b]:
+                    kpool[pg, :, sl] = kc[b, :, t]
+                    vpool[pg, :, sl] = vc[b, :, t]
+    if token_major:    # same values stored [page, slot, head, d], read through a strided view
+        kpool = np.ascontiguousarray(kpool.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
+        vpool = np.ascontiguousarray(vpool.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
+    O, L = decode_ref(q, kc, vc, lens, 0.3)
+    Op, Lp = paged_decode_ref(q, kpool, vpool, table, lens, 0.3)
+    assert np.array_equal(O, Op) and np.array_equal(L, Lp)
+
+
+@pytest.mark.parametrize("ps,layout", [(16, "head"), (24, "token"), (64, "token")])
+def test_paged_workload_holds_the_decode_values(ps, layout):
+    from io_aware_flashattention_amd import workloads as W
+    cfg = W.DecodeConfig("paged_pin", 3, 8, 2, 1, 200, 128, 777)
+    lens = np.array([200, 1, 77], dtype=np.int32)
+    q, kc, vc, _ = W.make_decode_inputs(cfg, lengths=lens)
+    q2, kp, vp, table, lens2 = W.make_paged_decode_inputs(cfg, ps, layout=layout, lengths=lens)
+    assert np.array_equal(q, q2) and np.array_equal(lens, lens2)
+    view = (lambda x: x) if layout == "head" else (lambda x: x.transpose(0, 2, 1, 3))
+    for b in range(cfg.batch):
+        n = int(lens[b])
+        assert np.array_equal(paged_rows(view(kp), table, b, n), kc[b, :, :n])
+        assert np.array_equal(paged_rows(view(vp), table, b, n), vc[b, :, :n])
+    nblk = [-(-int(n) // ps) for n in lens]
+    used = np.concatenate([table[b, :nblk[b]] for b in range(cfg.batch)])
+    assert len(set(used.tolist())) == len(used) == kp.shape[0] - 1     # distinct pages plus one pad page
+    pad_page = (set(range(kp.shape[0])) - set(used.tolist())).pop()
+    assert np.all(kp[pad_page] == W.BF16_NAN)
+    for b in range(cfg.batch):
+        assert np.all(table[b, nblk[b]:] == pad_page)
