@@ -172,8 +172,8 @@ FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_c
  *
  * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
  * page_size >= 16 (a 32-key block then spans at most three pages); pointers
- * 16-byte aligned; page strides multiples of 8 elements. Otherwise
- * FA_ERR_UNSUPPORTED.
+ * 16-byte aligned; page strides multiples of 8 elements; page_size *
+ * page_stride[2] < 2^31 elements. Otherwise FA_ERR_UNSUPPORTED.
  */
 FA_API fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                             const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,

@@ -80,6 +80,8 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
     return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: q, pages, o and workspace must be 16-byte aligned");
   for (int i = 0; i < 3; ++i)
     if (page_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: page strides must be multiples of 8 elements");
+  if ((int64_t)page_size * page_stride[2] >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: page_size * slot stride must stay below 2^31 elements");
   const int max_seqlen = max_blocks_per_seq * page_size;
   const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim);
   if (!workspace || workspace_bytes < need)

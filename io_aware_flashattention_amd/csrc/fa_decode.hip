@@ -177,45 +177,63 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     if constexpr (PAGED) {
       const int ps = p.page_size;
       const int pg0 = c.pos / ps;
-      const int pgl = (c.end - 1) / ps;
-      const const_i32* bt = (const const_i32*)p.block_table + (int64_t)c.b * p.max_blocks;
-      pr.e0 = bt[pg0];
-      pr.e1 = bt[min(pg0 + 1, pgl)];
-      pr.e2 = bt[min(pg0 + 2, pgl)];
       pr.off = c.pos - pg0 * ps;
       pr.lim = c.end - 1 - pg0 * ps;
+      // pages past the piece's last key are not looked up (their entries may be stale)
+      const int n1 = pr.lim >= ps ? 1 : 0, n2 = pr.lim >= 2 * ps ? 2 : n1;
+      const const_i32* bt = (const const_i32*)p.block_table + (int64_t)c.b * p.max_blocks + pg0;
+      pr.e0 = bt[0];
+      pr.e1 = bt[n1];
+      pr.e2 = bt[n2];
     }
     return pr;
   };
   auto issue = [&](const Cursor& c, int st, const PageRun& pr) {
     const __bf16* kp = reinterpret_cast<const __bf16*>(p.k);
     const __bf16* vp = reinterpret_cast<const __bf16*>(p.v);
-    int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
-    int64_t base1 = 0, base2 = 0;
+    __bf16* dst = smem + st * 2 * BLK;
     if constexpr (PAGED) {
+      // wave-uniform (page, kv head) bases of the block's pages; each lane then
+      // picks its row's page with two compares and adds slot * row stride
+      // (32-bit: page_size * stride < 2^31 is checked on the host)
+      const int ps = p.page_size;
       const int top = p.num_pages - 1;
       const int64_t hofs = (int64_t)c.kvh * p.kv_stride[1];
-      base = (int64_t)min(max(pr.e0, 0), top) * p.kv_stride[0] + hofs;
-      base1 = (int64_t)min(max(pr.e1, 0), top) * p.kv_stride[0] + hofs;
-      base2 = (int64_t)min(max(pr.e2, 0), top) * p.kv_stride[0] + hofs;
-    }
-    const int last = c.end - 1;
+      const __bf16* k0 = kp + (int64_t)min(max(pr.e0, 0), top) * p.kv_stride[0] + hofs;
+      const __bf16* k1 = kp + (int64_t)min(max(pr.e1, 0), top) * p.kv_stride[0] + hofs;
+      const __bf16* k2 = kp + (int64_t)min(max(pr.e2, 0), top) * p.kv_stride[0] + hofs;
+      // opaque to the optimiser, which would otherwise select the raw entries
+      // per lane and redo the clamp and the 64-bit products in vector registers
+      asm("" : "+s"(k0), "+s"(k1), "+s"(k2));
+      const intptr_t dvk = reinterpret_cast<intptr_t>(vp) - reinterpret_cast<intptr_t>(kp);
+      const int rs = (int)p.kv_stride[2];
+      const int o = pr.off + drow;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + drow;
-      int64_t row;
-      if constexpr (PAGED) {
-        const int ps = p.page_size;
-        const int kr = min(pr.off + r, pr.lim);           // slot counted from the first page
-        const int j = (kr >= ps) + (kr >= 2 * ps);
-        row = (j == 0 ? base : j == 1 ? base1 : base2) + (int64_t)(kr - j * ps) * p.kv_stride[2];
-      } else {
-        row = base + (int64_t)min(c.pos + r, last) * p.kv_stride[2];
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + drow;
+        const int kr = min(o + 4 * i, pr.lim);             // slot counted from the first page
+        const bool c1 = kr >= ps, c2 = kr >= 2 * ps;
+        int slot = c1 ? kr - ps : kr;
+        slot = c2 ? slot - ps : slot;
+        const __bf16* row = (c2 ? k2 : c1 ? k1 : k0) + (uint32_t)(slot * rs);
+        const __bf16* vrow = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(row) + dvk);
+        __builtin_amdgcn_global_load_lds((const void*)(row + 8 * (dchunk ^ kswz_d(r))), (lds_void*)(dst + i * 512),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (dchunk ^ vswz_d(r))),
+                                         (lds_void*)(dst + BLK + i * 512), 16, 0, 0);
       }
-      __bf16* dk = smem + st * 2 * BLK + i * 512;
-      __builtin_amdgcn_global_load_lds((const void*)(kp + row + 8 * (dchunk ^ kswz_d(r))), (lds_void*)dk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + row + 8 * (dchunk ^ vswz_d(r))), (lds_void*)(dk + BLK), 16,
-                                       0, 0);
+    } else {
+      const int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
+      const int last = c.end - 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + drow;
+        const int64_t row = base + (int64_t)min(c.pos + r, last) * p.kv_stride[2];
+        __builtin_amdgcn_global_load_lds((const void*)(kp + row + 8 * (dchunk ^ kswz_d(r))),
+                                         (lds_void*)(dst + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vp + row + 8 * (dchunk ^ vswz_d(r))),
+                                         (lds_void*)(dst + BLK + i * 512), 16, 0, 0);
+      }
     }
   };
 

@@ -137,6 +137,7 @@ def _paged(**kw):
     (dict(ps=8), 2, "page_size"),
     (dict(v=FAKE + 0x200004), 2, "aligned"),
     (dict(pst=(4096, 2048, 132)), 2, "multiples"),
+    (dict(ps=1024, pst=(1 << 32, 1 << 22, 1 << 21)), 2, "2^31"),
     (dict(wsb=100), 3, "workspace"),
 ])
 def test_decode_paged_rejects_before_launch(kw, status, needle):
