@@ -19,6 +19,9 @@ Recipe (the pages give shapes and "drawn from N(0,1)" but no generator):
   [1024, 32768] inclusive; cache rows past a sequence's length are filled
   with a pad value (NaN in tests, so over-reads poison the result; zero in
   the benchmark);
+* packed (varlen) prefill inputs draw each sequence's length uniformly from
+  the config's [min, max] (stream ``[seed, tag=5]``) and store every
+  sequence's heads token-major at its cumulative offset;
 * the paged form of a decode workload holds the same token values in a pool
   of fixed-size pages: every sequence gets ceil(L_b / page_size) pages, the
   pages of all sequences are a random permutation of the pool (stream
@@ -271,6 +274,68 @@ def make_paged_decode_inputs(cfg: DecodeConfig, page_size: int, layout: str = "h
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(run, jobs))
     return q, kp, vp, table, lens
+
+
+@dataclass(frozen=True)
+class VarlenConfig:
+    """Packed prefill: sequences concatenated on the token axis (cu_seqlens)."""
+    name: str
+    n_seqs: int
+    heads_q: int
+    heads_kv: int
+    min_len: int
+    max_len: int
+    head_dim: int
+    causal: bool
+    window: int          # sliding window W (row r sees keys r-W..r), -1 for none
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
+# Packed-batch and sliding-window prefill on the GQA shape of the decode and
+# long-context workloads: a mix of lengths, and the pages' window example
+# (8192 tokens, keys at most 1024 positions behind the row).
+VARLEN_CONFIGS = {
+    "c6_varlen_causal": VarlenConfig("c6_varlen_causal", 16, 64, 8, 1, 8192, 128, True, -1, 20260006),
+    "c7_window_8k": VarlenConfig("c7_window_8k", 1, 64, 8, 8192, 8192, 128, True, 1024, 20260007),
+}
+
+
+def varlen_lengths(cfg: VarlenConfig) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64([cfg.seed, TAG_LENS]))
+    return rng.integers(cfg.min_len, cfg.max_len, size=cfg.n_seqs, endpoint=True).astype(np.int32)
+
+
+def make_varlen_inputs(heads_q: int, heads_kv: int, head_dim: int, lengths, seed: int, dtype: str = "bf16"):
+    """Packed q [total, Hq, d], k/v [total, Hkv, d] (bf16 bits) and cu_seqlens [n+1] int32.
+
+    Sequence b's head h is the slice keyed [seed, tag, b, h], as for the dense
+    workloads, laid out token-major.
+    """
+    lens = np.asarray(lengths, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    conv = (lambda x: x) if dtype == "fp32" else f32_to_bf16_bits
+    dt = np.float32 if dtype == "fp32" else np.uint16
+    q = np.empty((total, heads_q, head_dim), dtype=dt)
+    k = np.empty((total, heads_kv, head_dim), dtype=dt)
+    v = np.empty_like(k)
+    jobs = [("q", b, h) for b in range(len(lens)) for h in range(heads_q)]
+    jobs += [(w, b, h) for w in ("k", "v") for b in range(len(lens)) for h in range(heads_kv)]
+    dst = {"q": q, "k": k, "v": v}
+    tags = {"q": TAG_Q, "k": TAG_K, "v": TAG_V}
+
+    def run(job):
+        w, b, h = job
+        n = int(lens[b])
+        dst[w][cu[b]:cu[b] + n, h] = conv(_normal_f32(seed, tags[w], b, h, (n, head_dim)))
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(run, jobs))
+    return q, k, v, cu
 
 
 def to_f64(x: np.ndarray) -> np.ndarray:

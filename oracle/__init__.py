@@ -5,7 +5,8 @@ this package. The product path never does.
 """
 from .attention import (attention_ref, block_summary, decode_ref, merge_lse,
                         merge_summaries, paged_decode_ref, paged_rows, split_decode_ref,
-                        stream_attention)
+                        stream_attention, varlen_ref)
 
 __all__ = ["attention_ref", "stream_attention", "block_summary", "merge_summaries",
-           "merge_lse", "decode_ref", "split_decode_ref", "paged_rows", "paged_decode_ref"]
+           "merge_lse", "decode_ref", "split_decode_ref", "paged_rows", "paged_decode_ref",
+           "varlen_ref"]

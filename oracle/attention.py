@@ -30,6 +30,15 @@ What it computes, and where the pages define it:
   FlashAttention Reduces HBM Traffic Exactly" section "Why softmax does not
   prevent tiling"; "FlashAttention Explained" section "Decoding, Paged and
   Split-KV Variants".)
+* ``attention_ref(..., window=W)`` -- the sliding-window mask on top of the
+  causal one: row r sees keys r - W .. r (the pages' example keeps a key when
+  q_idx >= kv_idx and q_idx - kv_idx <= W; "FlashAttention Explained",
+  section "FlexAttention"; "FlashAttention and Why Attention Is a
+  Memory-Traffic Problem": windows skip every block outside them).
+* ``varlen_ref`` -- packed variable-length batches: sequences concatenated on
+  the token axis with cumulative offsets cu_seqlens, each attending only to
+  itself ("FlashAttention Explained", section "Trade-offs, Gotchas, and What
+  Goes Wrong": varlen kernels skip pad tokens given cumulative lengths).
 * ``decode_ref`` -- single-token decode: the same attention for one query row
   per head over the first L_b cached keys of each sequence.
 * ``paged_rows`` / ``paged_decode_ref`` -- the same decode over a paged cache:
@@ -80,14 +89,18 @@ def _softmax_rows(S: np.ndarray):
 
 
 def attention_ref(q, k, v, scale: float, causal: bool = False, q_positions=None,
-                  row_block: int = _ROW_BLOCK):
+                  row_block: int = _ROW_BLOCK, window=None):
     """Materialising attention in fp64.
 
     q: [B, Hq, Nq, d]; k: [B, Hkv, Nk, d]; v: [B, Hkv, Nk, dv]; Hq % Hkv == 0.
     q_positions: absolute key-axis position of each query row (default 0..Nq-1),
-    used only by the causal mask, so a subset of rows can be checked alone.
+    used only by the masks, so a subset of rows can be checked alone.
+    window: sliding-window size W (with ``causal``): key c is also masked when
+    it lies more than W positions behind the row, so a row sees keys
+    [row - W, row].
     Returns O [B, Hq, Nq, dv] and LSE [B, Hq, Nq], both fp64.
     """
+    assert window is None or (causal and window >= 0), "a window is defined on top of the causal mask"
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, Hq, Nq, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
@@ -108,10 +121,44 @@ def attention_ref(q, k, v, scale: float, causal: bool = False, q_positions=None,
                 S = scale * (q[b, h, r0:r1] @ K.T)
                 if causal:
                     S[cols[None, :] > pos[r0:r1, None]] = -np.inf
+                if window is not None:
+                    S[cols[None, :] < pos[r0:r1, None] - window] = -np.inf
                 P, m, l = _softmax_rows(S)
                 O[b, h, r0:r1] = P @ V
                 live = l > 0
                 L[b, h, r0:r1][live] = m[live] + np.log(l[live])
+    return O, L
+
+
+def varlen_ref(q, k, v, cu_seqlens, scale: float, causal: bool = False, window=None, rows=None):
+    """Attention over packed sequences.
+
+    q: [total, Hq, d]; k, v: [total, Hkv, d] (token-major, all sequences
+    concatenated); cu_seqlens: [batch + 1] offsets, sequence b owning tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k and v alike, with positions
+    counted from its own start. ``rows`` optionally restricts the work to a
+    list of packed token indices (others stay O = 0, LSE = -inf).
+    Returns O [total, Hq, dv] and LSE [Hq, total] in fp64.
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    total, Hq, d = q.shape
+    cu = [int(x) for x in cu_seqlens]
+    O = np.zeros((total, Hq, v.shape[2]))
+    L = np.full((Hq, total), -np.inf)
+    want = None if rows is None else set(int(r) for r in rows)
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 <= s0:
+            continue
+        local = np.arange(s1 - s0) if want is None else np.array([r - s0 for r in range(s0, s1) if r in want])
+        if local.size == 0:
+            continue
+        qb = _as64(q[s0 + local]).transpose(1, 0, 2)[None]         # [1, Hq, n_rows, d]
+        kb = _as64(k[s0:s1]).transpose(1, 0, 2)[None]
+        vb = _as64(v[s0:s1]).transpose(1, 0, 2)[None]
+        ob, lb = attention_ref(qb, kb, vb, scale, causal=causal, q_positions=local, window=window)
+        O[s0 + local] = ob[0].transpose(1, 0, 2)
+        L[:, s0 + local] = lb[0]
     return O, L
 
 

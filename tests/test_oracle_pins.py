@@ -10,7 +10,7 @@ from hypothesis import given, settings
 from hypothesis import strategies as st
 
 from oracle import (attention_ref, block_summary, decode_ref, merge_lse, merge_summaries,
-                    paged_decode_ref, paged_rows, split_decode_ref, stream_attention)
+                    paged_decode_ref, paged_rows, split_decode_ref, stream_attention, varlen_ref)
 from tests.conftest import golden
 
 
@@ -439,3 +439,118 @@ def test_paged_workload_holds_the_decode_values(ps, layout):
     assert np.all(kp[pad_page] == W.BF16_NAN)
     for b in range(cfg.batch):
         assert np.all(table[b, nblk[b]:] == pad_page)
+
+
+# ---------------------------------------------------------- sliding window --
+
+@pytest.mark.parametrize("W", [0, 1, 5, 17, 100])
+def test_window_closed_form_with_zero_query(W):
+    """q = 0 gives equal weights over the visible keys: with V[c] = c the output
+    of row r is the mean of lo..r, lo = max(0, r - W), and LSE = ln(r - lo + 1)."""
+    N = 40
+    q = np.zeros((1, 1, N, 4))
+    k = np.random.default_rng(W).standard_normal((1, 1, N, 4))
+    v = np.arange(N, dtype=np.float64).reshape(1, 1, N, 1)
+    O, L = attention_ref(q, k, v, 0.7, causal=True, window=W)
+    for r in range(N):
+        lo = max(0, r - W)
+        assert abs(O[0, 0, r, 0] - (lo + r) / 2) < 1e-12
+        assert abs(L[0, 0, r] - math.log(r - lo + 1)) < 1e-12
+
+
+def test_window_brute_force():
+    rng = np.random.default_rng(61)
+    N, d, W, scale = 13, 3, 4, 0.6
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, 2))
+    O, L = attention_ref(q[None, None], k[None, None], v[None, None], scale, causal=True, window=W)
+    for r in range(N):
+        vis = [c for c in range(N) if c <= r and r - c <= W]
+        sc = [scale * sum(q[r, i] * k[c, i] for i in range(d)) for c in vis]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = sum(w)
+        for j in range(2):
+            assert abs(O[0, 0, r, j] - sum(wi * v[c, j] for wi, c in zip(w, vis)) / tot) < 1e-12
+        assert abs(L[0, 0, r] - (mx + math.log(tot))) < 1e-12
+
+
+def test_window_limits():
+    rng = np.random.default_rng(62)
+    q, k, v = (rng.standard_normal((1, 2, 30, 8)) for _ in range(3))
+    Oc, Lc = attention_ref(q, k, v, 0.3, causal=True)
+    Ow, Lw = attention_ref(q, k, v, 0.3, causal=True, window=29)
+    assert np.array_equal(Oc, Ow) and np.array_equal(Lc, Lw)          # a window as long as the sequence
+    O0, L0 = attention_ref(q, k, v, 0.3, causal=True, window=0)     # each row sees only itself
+    assert np.array_equal(O0, v)
+    assert np.allclose(L0, 0.3 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-13)
+    with pytest.raises(AssertionError):
+        attention_ref(q, k, v, 0.3, causal=False, window=4)
+
+
+# ------------------------------------------------------ packed sequences ----
+
+def _packed(rng, lens, Hq=4, Hkv=2, d=8):
+    total = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return (rng.standard_normal((total, Hq, d)), rng.standard_normal((total, Hkv, d)),
+            rng.standard_normal((total, Hkv, d)), cu)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 3)])
+def test_varlen_brute_force(causal, window):
+    """Every packed row attends to the keys of its own sequence only: the rule is
+    written over global token indices with a sequence-id array."""
+    rng = np.random.default_rng(71)
+    lens = [5, 0, 1, 7]
+    q, k, v, cu = _packed(rng, lens, Hq=2, Hkv=1, d=3)
+    O, L = varlen_ref(q, k, v, cu, 0.8, causal=causal, window=window)
+    seq = np.repeat(np.arange(len(lens)), lens)
+    start = cu[seq]
+    for r in range(len(seq)):
+        for h in range(2):
+            vis = [c for c in range(len(seq)) if seq[c] == seq[r]
+                   and (not causal or c <= r) and (window is None or r - c <= window)]
+            sc = [0.8 * sum(q[r, h, i] * k[c, 0, i] for i in range(3)) for c in vis]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for j in range(3):
+                assert abs(O[r, h, j] - sum(wi * v[c, 0, j] for wi, c in zip(w, vis)) / tot) < 1e-12
+            assert abs(L[h, r] - (mx + math.log(tot))) < 1e-12
+    assert np.all(start <= np.arange(len(seq)))
+
+
+def test_varlen_sequences_are_isolated_and_order_free():
+    rng = np.random.default_rng(72)
+    lens = [9, 4, 12]
+    q, k, v, cu = _packed(rng, lens)
+    O, L = varlen_ref(q, k, v, cu, 0.5, causal=True)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[1]:cu[2]] += 3.0                      # change only sequence 1
+    v2[cu[1]:cu[2]] -= 1.0
+    O2, L2 = varlen_ref(q, k2, v2, cu, 0.5, causal=True)
+    for b in (0, 2):
+        sl = slice(cu[b], cu[b + 1])
+        assert np.array_equal(O[sl], O2[sl]) and np.array_equal(L[:, sl], L2[:, sl])
+    assert not np.allclose(O[cu[1]:cu[2]], O2[cu[1]:cu[2]])
+    order = [2, 0, 1]                           # pack the same sequences in another order
+    idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in order])
+    cu3 = np.concatenate([[0], np.cumsum([lens[b] for b in order])])
+    O3, L3 = varlen_ref(q[idx], k[idx], v[idx], cu3, 0.5, causal=True)
+    assert np.array_equal(O3, O[idx]) and np.array_equal(L3, L[:, idx])
+
+
+def test_varlen_single_sequence_is_dense_and_rows_subset():
+    rng = np.random.default_rng(73)
+    q, k, v, cu = _packed(rng, [33], Hq=4, Hkv=2, d=8)
+    O, L = varlen_ref(q, k, v, cu, 0.4, causal=True, window=7)
+    Od, Ld = attention_ref(q.transpose(1, 0, 2)[None], k.transpose(1, 0, 2)[None], v.transpose(1, 0, 2)[None],
+                           0.4, causal=True, window=7)
+    assert np.array_equal(O, Od[0].transpose(1, 0, 2)) and np.array_equal(L, Ld[0])
+    rows = [0, 5, 32]
+    Os, Ls = varlen_ref(q, k, v, cu, 0.4, causal=True, window=7, rows=rows)
+    assert np.array_equal(Os[rows], O[rows]) and np.array_equal(Ls[:, rows], L[:, rows])
+    others = [r for r in range(33) if r not in rows]
+    assert np.all(Os[others] == 0) and np.all(np.isneginf(Ls[:, others]))
