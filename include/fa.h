@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of libfa, an MI355X (gfx950) FlashAttention forward pass.
  *
- * Two operations:
+ * Operations:
  *
  *   fa_fwd     exact softmax attention O = softmax(scale * Q K^T + mask) V for
  *              prefill, computed tile by tile with a running row maximum and
@@ -15,12 +15,16 @@
  *              Tiling, Online Softmax and FP8 on Hopper", section "Why the
  *              statistics are cheap to store".)
  *
+ *   fa_fwd_varlen  the same over packed variable-length sequences, with an
+ *              optional sliding-window mask.
+ *
  *   fa_decode  single-token decode against a KV cache, with the key axis split
  *              across workgroups; every split writes a partial output and its
  *              log-sum-exp, and a second small kernel merges the partials
  *              ("FlashAttention Explained", section "Decoding, Paged and
  *              Split-KV Variants"; "FlashAttention and GPU Data Movement",
- *              section 6.1).
+ *              section 6.1). fa_decode_paged reads the cache through a
+ *              block table of fixed-size pages.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
@@ -99,6 +103,49 @@ FA_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, 
                    const int64_t v_stride[3], const int64_t o_stride[3],
                    fa_dtype_t in_dtype, fa_dtype_t out_dtype, fa_mask_t mask,
                    float softmax_scale, void* stream);
+
+/*
+ * fa_fwd_varlen -- prefill over a packed batch of variable-length sequences,
+ * optionally with a sliding-window mask.
+ *
+ * Sequences are concatenated on the token axis and described by cumulative
+ * offsets, so no work is spent on padding ("FlashAttention Explained: IO-Aware
+ * Attention, Tiling, Online Softmax and FP8 on Hopper", section "Trade-offs,
+ * Gotchas, and What Goes Wrong"). Sequence b owns tokens cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1 of q, k, v and o alike and attends only to itself, with
+ * positions counted from its own first token. The sliding window is the
+ * causal mask restricted to the last window+1 keys: key c is visible to row r
+ * iff c <= r and r - c <= window (same page, section "FlexAttention"; key
+ * tiles wholly outside every row's window are skipped, as the causal mask
+ * skips future tiles: "FlashAttention and Why Attention Is a Memory-Traffic
+ * Problem").
+ *
+ * q   [total_tokens, heads_q,  head_dim] bf16, strides q_stride = {token, head}
+ * k   [total_tokens, heads_kv, head_dim] bf16, strides k_stride = {token, head}
+ * v   [total_tokens, heads_kv, head_dim] bf16, strides v_stride = {token, head}
+ * o   [total_tokens, heads_q,  head_dim] out_dtype, strides o_stride = {token, head}
+ * lse [heads_q, total_tokens] float32, contiguous; may be NULL.
+ * cu_seqlens  DEVICE int32 [batch + 1], non-decreasing, cu_seqlens[0] = 0 and
+ *             cu_seqlens[batch] <= total_tokens. Entries are clamped into
+ *             [0, total_tokens] on the device, so no access leaves the buffers.
+ * max_seqlen  an upper bound of every sequence's length (sizes the grid); rows
+ *             of a longer sequence past max_seqlen are not written.
+ * mask        FA_MASK_NONE or FA_MASK_CAUSAL (within each sequence).
+ * window      -1 for none, else >= 0 and only with FA_MASK_CAUSAL.
+ *
+ * Supported: bf16 inputs; head_dim 64 or 128; heads_q % heads_kv == 0;
+ * 16-byte aligned pointers; strides multiples of 16 bytes; k/v token strides at
+ * most 2^24 elements. Otherwise FA_ERR_UNSUPPORTED. o must not overlap q, k, v.
+ * With uniform lengths and a token-major layout this computes exactly what
+ * fa_fwd computes on the same memory (same kernels, same tiles, same bits).
+ */
+FA_API fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                          int32_t total_tokens, int32_t max_seqlen, int32_t head_dim,
+                          const int64_t q_stride[2], const int64_t k_stride[2],
+                          const int64_t v_stride[2], const int64_t o_stride[2],
+                          fa_dtype_t out_dtype, fa_mask_t mask, int32_t window, float softmax_scale,
+                          void* stream);
 
 /*
  * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes:

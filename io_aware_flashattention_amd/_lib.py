@@ -21,8 +21,8 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string",
-            "fa_last_error_message")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
+            "fa_status_string", "fa_last_error_message")
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
 _lib = None
@@ -46,6 +46,11 @@ def load():
     lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                            ctypes.c_float, _vp]
+    lib.fa_fwd_varlen.restype = ctypes.c_int
+    lib.fa_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,             # q, k, v, o, lse, cu_seqlens
+                                  _i32, _i32, _i32, _i32, _i32, _i32,       # batch, Hq, Hkv, total, max_seqlen, d
+                                  _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, _i32,
+                                  ctypes.c_float, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
     lib.fa_decode.restype = ctypes.c_int
@@ -114,6 +119,50 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                     B, Hq, Hkv, N, Nk, d, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
                     _dtype_code(q.dtype), _dtype_code(out.dtype),
                     FA_MASK_CAUSAL if causal else FA_MASK_NONE, float(scale), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def _strides2(t: torch.Tensor):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [tokens, heads, d] tensor with contiguous last dimension")
+    return (ctypes.c_int64 * 2)(t.stride(0), t.stride(1))
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+               causal: bool = False, window: int | None = None, scale: float | None = None,
+               out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | bool | None = True):
+    """Packed prefill. q [total,Hq,d], k/v [total,Hkv,d] bf16 on the GPU; cu_seqlens int32 [B+1]
+    on the GPU; ``window`` (causal only): row r sees keys r-window .. r.
+
+    Returns (O [total,Hq,d], LSE float32 [Hq,total] or None).
+    """
+    lib = load()
+    total, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must be bfloat16")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    if k.shape[0] != total or v.shape[0] != total:
+        raise ValueError("q, k and v must hold the same packed tokens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((total, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (Hq, total)):
+        raise ValueError("lse must be a contiguous float32 [Hq, total] tensor")
+    st = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr() if lse is not None else None, cu_seqlens.data_ptr(),
+                           cu_seqlens.numel() - 1, Hq, Hkv, total, int(max_seqlen), d,
+                           _strides2(q), _strides2(k), _strides2(v), _strides2(out), _dtype_code(out.dtype),
+                           FA_MASK_CAUSAL if causal else FA_MASK_NONE, -1 if window is None else int(window),
+                           float(scale), _stream(q.device))
     _check(st)
     return out, lse
 

@@ -190,8 +190,88 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.causal = mask == FA_MASK_CAUSAL;
   p.in_fp32 = in_dtype == FA_DTYPE_FP32;
   p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  p.cu_seqlens = nullptr;
+  p.total = 0;
+  p.window = -1;
   hipError_t e = fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                          int32_t total_tokens, int32_t max_seqlen, int32_t head_dim,
+                          const int64_t q_stride[2], const int64_t k_stride[2],
+                          const int64_t v_stride[2], const int64_t o_stride[2],
+                          fa_dtype_t out_dtype, fa_mask_t mask, int32_t window, float softmax_scale,
+                          void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: q, k, v, o and cu_seqlens must be non-null");
+  if (!q_stride || !k_stride || !v_stride || !o_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: stride arrays must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || total_tokens <= 0 || max_seqlen <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_fwd_varlen: sizes must be positive (batch=%d heads_q=%d heads_kv=%d total=%d max_seqlen=%d head_dim=%d)",
+                batch, heads_q, heads_kv, total_tokens, max_seqlen, head_dim);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: softmax_scale must be finite and positive (got %g)",
+                (double)softmax_scale);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: unknown out_dtype %d", (int)out_dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: unknown mask %d", (int)mask);
+  if (window < -1) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: window must be -1 (none) or >= 0");
+  for (int i = 0; i < 2; ++i)
+    if (q_stride[i] < 0 || k_stride[i] < 0 || v_stride[i] < 0 || o_stride[i] < 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: strides must be non-negative");
+
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: head_dim %d not supported (64 or 128)", head_dim);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: heads_q (%d) must be a multiple of heads_kv (%d)", heads_q,
+                heads_kv);
+  if (window >= 0 && mask != FA_MASK_CAUSAL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: a sliding window needs the causal mask");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: q, k, v and o must be 16-byte aligned");
+  for (int i = 0; i < 2; ++i)
+    if (q_stride[i] % 8 || k_stride[i] % 8 || v_stride[i] % 8 || o_stride[i] % (out_dtype == FA_DTYPE_BF16 ? 8 : 4))
+      return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: strides must be multiples of 16 bytes");
+  if (k_stride[0] > (int64_t(1) << 24) || v_stride[0] > (int64_t(1) << 24))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: k/v token strides above 2^24 elements are not supported");
+  // byte spans as [1, heads, total, d] tensors with {0, head, token} strides
+  const int64_t out_b = out_dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const int64_t qs3[3] = {0, q_stride[1], q_stride[0]}, ks3[3] = {0, k_stride[1], k_stride[0]};
+  const int64_t vs3[3] = {0, v_stride[1], v_stride[0]}, os3[3] = {0, o_stride[1], o_stride[0]};
+  uintptr_t o0, o1, a0, a1;
+  span(o, os3, 1, heads_q, total_tokens, head_dim, out_b, &o0, &o1);
+  span(q, qs3, 1, heads_q, total_tokens, head_dim, 2, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: o overlaps q");
+  span(k, ks3, 1, heads_kv, total_tokens, head_dim, 2, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: o overlaps k");
+  span(v, vs3, 1, heads_kv, total_tokens, head_dim, 2, &a0, &a1);
+  if (overlap(o0, o1, a0, a1)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_varlen: o overlaps v");
+  const int64_t n_qtiles = (max_seqlen + 63) / 64;        // bound over every kernel's row tile
+  if ((int64_t)batch * heads_q * n_qtiles > 0x7fffffffLL || (int64_t)heads_q * total_tokens > (int64_t(1) << 40))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: problem too large for one launch");
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_stride[0] = 0; p.q_stride[1] = q_stride[1]; p.q_stride[2] = q_stride[0];
+  p.k_stride[0] = 0; p.k_stride[1] = k_stride[1]; p.k_stride[2] = k_stride[0];
+  p.v_stride[0] = 0; p.v_stride[1] = v_stride[1]; p.v_stride[2] = v_stride[0];
+  p.o_stride[0] = 0; p.o_stride[1] = o_stride[1]; p.o_stride[2] = o_stride[0];
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+  p.seqlen_q = max_seqlen; p.seqlen_k = max_seqlen; p.head_dim = head_dim;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = mask == FA_MASK_CAUSAL;
+  p.in_fp32 = false;
+  p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  p.cu_seqlens = cu_seqlens;
+  p.total = total_tokens;
+  p.window = window;
+  hipError_t e = fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -96,6 +96,46 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Offsets (elements) of one (sequence, query head) in q, k, v, o and the LSE,
+// and its lengths. A packed batch reads its offsets at wave-uniform
+// addresses (scalar loads); they are clamped into [0, total] so a bad offset
+// array cannot move an access outside the packed buffers.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+struct SeqView {
+  int64_t q, k, v, o, lse;
+  int nq, nk;
+};
+
+__device__ __forceinline__ SeqView seq_view(const FwdParams& p, int b, int hq, int kvh) {
+  SeqView s;
+  int64_t tq = 0, tk = 0, tv = 0, to = 0;
+  if (p.cu_seqlens != nullptr) {
+    const const_i32* cu = (const const_i32*)p.cu_seqlens;
+    const int s0 = min(max(cu[b], 0), p.total);
+    const int s1 = min(max(cu[b + 1], s0), p.total);
+    s.nq = s.nk = s1 - s0;
+    tq = (int64_t)s0 * p.q_stride[2];
+    tk = (int64_t)s0 * p.k_stride[2];
+    tv = (int64_t)s0 * p.v_stride[2];
+    to = (int64_t)s0 * p.o_stride[2];
+    s.lse = (int64_t)hq * p.total + s0;
+  } else {
+    s.nq = p.seqlen_q;
+    s.nk = p.seqlen_k;
+    tq = (int64_t)b * p.q_stride[0];
+    tk = (int64_t)b * p.k_stride[0];
+    tv = (int64_t)b * p.v_stride[0];
+    to = (int64_t)b * p.o_stride[0];
+    s.lse = ((int64_t)b * p.heads_q + hq) * p.seqlen_q;
+  }
+  s.q = tq + (int64_t)hq * p.q_stride[1];
+  s.k = tk + (int64_t)kvh * p.k_stride[1];
+  s.v = tv + (int64_t)kvh * p.v_stride[1];
+  s.o = to + (int64_t)hq * p.o_stride[1];
+  return s;
+}
+
 }  // namespace
 
 namespace detail {
@@ -137,16 +177,22 @@ void fwd_bf16_kernel(const FwdParams p) {
   const int hq = kvh * p.group + g;
   const int qt = CAUSAL ? p.n_qtiles - 1 - t : t;
 
-  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_stride[0] + hq * p.q_stride[1];
-  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + b * p.k_stride[0] + kvh * p.k_stride[1];
-  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_stride[0] + kvh * p.v_stride[1];
+  const SeqView sv = seq_view(p, b, hq, kvh);
+  const int q0 = qt * BRW;
+  const int nq = sv.nq, nk = sv.nk;
+  if (q0 >= nq) return;                      // a packed sequence shorter than the longest (whole workgroup)
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + sv.q;
+  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + sv.k;
+  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + sv.v;
   const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
 
-  const int q0 = qt * BRW;
   const int wrow0 = q0 + wave * 32 * R;      // first row of this wave; block rb starts at wrow0 + 32 rb
-  const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int W = CAUSAL ? p.window : -1;      // sliding window (row r sees keys r-W .. r)
   const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;    // skip bound
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // tiles wholly behind every row's window are skipped too; tile indices
+  // below are counted from the workgroup's first needed tile jbase
+  const int jbase = W >= 0 ? max(0, q0 - W) / BC : 0;
+  const int ntiles = (kv_end + BC - 1) / BC - jbase;
 
   // ---- DMA plan: this lane's 16-byte chunk of each 1-KB write
   int dma_row[LPW], dma_k[LPW], dma_v[LPW];
@@ -159,7 +205,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     dma_v[i] = 8 * (pc ^ vswz_t<D>(r));
   }
   auto issue = [&](int tile, int ST) {
-    const int kv0 = tile * BC;
+    const int kv0 = (jbase + tile) * BC;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int key = min(kv0 + dma_row[i], nk - 1);
@@ -211,8 +257,10 @@ void fwd_bf16_kernel(const FwdParams p) {
     for (int i = 0; i < DBLK; ++i) o[rb][i] = f32x16{};
   }
 
-  // tiles this wave needs (under the causal mask, the rest lie in its future)
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 32 * R - 1) / BC + 1) : ntiles;
+  // tiles this wave needs: [lo_w, nt_w) (under the causal mask later tiles
+  // lie in its future, under a window earlier ones lie behind it)
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 32 * R - 1) / BC + 1 - jbase) : ntiles;
+  const int lo_w = W >= 0 ? max(0, wrow0 - W) / BC - jbase : 0;
 
   // S^T of one 64-key tile (K in stage ST) for the R row blocks: each K
   // fragment read once, used R times
@@ -232,17 +280,20 @@ void fwd_bf16_kernel(const FwdParams p) {
     }
   };
 
-  // diagonal / ragged tiles: -inf where the key is in the row's future or past the end
+  // diagonal / ragged / window-edge tiles: -inf where the key is in the row's
+  // future, past the end, or more than W behind the row
   auto mask = [&](int kv0, f32x16 (&a)[R][2]) {
-    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
+    const bool win = W >= 0 && kv0 < wrow0 + 32 * R - 1 - W;
+    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk) || win) {
 #pragma unroll
       for (int rb = 0; rb < R; ++rb) {
         const int row = wrow0 + 32 * rb + r32;
+        const int kmin = win ? row - W : -1;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
-          a[rb][0][jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : a[rb][0][jj];
-          a[rb][1][jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : a[rb][1][jj];
+          a[rb][0][jj] = ((CAUSAL && k0 > row) || k0 >= nk || k0 < kmin) ? kNegInf : a[rb][0][jj];
+          a[rb][1][jj] = ((CAUSAL && k1 > row) || k1 >= nk || k1 < kmin) ? kNegInf : a[rb][1][jj];
         }
       }
     }
@@ -344,9 +395,9 @@ void fwd_bf16_kernel(const FwdParams p) {
   if (STAGES > 3 && 2 < ntiles) wait_vmcnt<2 * LPW>();   // tiles 0 and 1 landed, 2 may fly
   else wait_vmcnt<0>();
   __syncthreads();
-  if (0 < nt_w) {
+  if (lo_w == 0 && 0 < nt_w) {
     scores(0, cur);
-    mask(0, cur);
+    mask(jbase * BC, cur);
     move_base(cur);
   }
 
@@ -359,13 +410,13 @@ void fwd_bf16_kernel(const FwdParams p) {
       __syncthreads();                       // ... for every wave; tile j-1's stage is free
     }
     if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, (SV + STAGES - 1) % STAGES);
-    const bool act = j < nt_w, nxt = j + 1 < nt_w;
+    const bool act = j >= lo_w && j < nt_w, nxt = j + 1 >= lo_w && j + 1 < nt_w;
     bf16x8 pb[R][4];
     f32x16 nx[R][2];
     if (act && nxt) {
       scores(SK, nx);                        // matrix cores ...
       weights(cur, pb);                      // ... alongside the exponentials
-      mask((j + 1) * BC, nx);
+      mask((jbase + j + 1) * BC, nx);
       accumulate(SV, pb);                    // matrix cores ...
       move_base(nx);                         // ... alongside the next maxima
 #pragma unroll
@@ -376,6 +427,10 @@ void fwd_bf16_kernel(const FwdParams p) {
     } else if (act) {                        // this wave's last tile
       weights(cur, pb);
       accumulate(SV, pb);
+    } else if (nxt) {                        // this wave's first tile (behind a window)
+      scores(SK, cur);
+      mask((jbase + j + 1) * BC, cur);
+      move_base(cur);
     }
   };
 
@@ -392,7 +447,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     const int row = wrow0 + 32 * rb + r32;
     if (row >= nq) continue;
     const float inv_l = l_o[rb] > 0.f ? 1.f / l_o[rb] : 0.f;
-    TOut* op = reinterpret_cast<TOut*>(p.o) + b * p.o_stride[0] + hq * p.o_stride[1] + (int64_t)row * p.o_stride[2];
+    TOut* op = reinterpret_cast<TOut*>(p.o) + sv.o + (int64_t)row * p.o_stride[2];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -410,7 +465,7 @@ void fwd_bf16_kernel(const FwdParams p) {
       }
     if (p.lse != nullptr && half == 0) {
       const float lse = l_run[rb] > 0.f ? (m_run[rb] + __log2f(l_run[rb])) * kLn2 : kNegInf;
-      p.lse[((int64_t)b * p.heads_q + hq) * nq + row] = lse;
+      p.lse[sv.lse + row] = lse;
     }
   }
 }
@@ -480,22 +535,29 @@ void fwd_pp_kernel(const FwdParams p) {
   const int hq = kvh * p.group + g;
   const int qt = CAUSAL ? p.n_qtiles - 1 - t : t;
 
-  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_stride[0] + hq * p.q_stride[1];
-  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + b * p.k_stride[0] + kvh * p.k_stride[1];
-  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_stride[0] + kvh * p.v_stride[1];
+  const SeqView sv = seq_view(p, b, hq, kvh);
+  const int q0 = qt * BRW;
+  const int nq = sv.nq, nk = sv.nk;
+  if (q0 >= nq) return;                      // a packed sequence shorter than the longest (whole workgroup)
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + sv.q;
+  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + sv.k;
+  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + sv.v;
   const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
 
-  const int q0 = qt * BRW;
   const int wrow0 = q0 + wave * 32;
   const int row = wrow0 + r32;
-  const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int W = CAUSAL ? p.window : -1;      // sliding window (row r sees keys r-W .. r)
   const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;
-  const int ntiles = (kv_end + BC - 1) / BC;
-  // Tiles this wave needs. Without the mask that is every tile, but the bound
-  // is still written in terms of the wave's rows (equal to ntiles since
-  // wrow0 >= 0): a wave-uniform bound lets the compiler turn the unit loop
-  // into uniform branches whose register allocation spills.
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1) : min(ntiles, (wrow0 + nk + BC - 1) / BC);
+  // Tile indices below count from the workgroup's first needed tile jbase
+  // (tiles wholly behind every row's window are never loaded).
+  const int jbase = W >= 0 ? max(0, q0 - W) / BC : 0;
+  const int ntiles = (kv_end + BC - 1) / BC - jbase;
+  // Tiles this wave needs: [lo_w, nt_w). Without the mask that is every
+  // tile, but the bound is still written in terms of the wave's rows (equal
+  // to ntiles since wrow0 >= 0): a wave-uniform bound lets the compiler turn
+  // the unit loop into uniform branches whose register allocation spills.
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1 - jbase) : min(ntiles, (wrow0 + nk + BC - 1) / BC);
+  const int lo_w = W >= 0 ? max(0, wrow0 - W) / BC - jbase : 0;
 
   // DMA plan: this lane's 16-byte chunk of each 1-KB write, as a byte offset
   // inside one key tile, so a load is a scalar tile base plus a 32-bit offset
@@ -513,7 +575,7 @@ void fwd_pp_kernel(const FwdParams p) {
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int tile, int ST) {
-    const int kv0 = tile * BC;
+    const int kv0 = (jbase + tile) * BC;
     const char* kb = reinterpret_cast<const char*>(kp + (int64_t)kv0 * ks2);
     const char* vb = reinterpret_cast<const char*>(vp + (int64_t)kv0 * vs2);
     __bf16* dst = smem + ST * 2 * TILE + wave_u * LPW * 512;
@@ -665,12 +727,14 @@ void fwd_pp_kernel(const FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
   auto softmax = [&](int kv0) {
-    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk)) {
+    const bool win = W >= 0 && kv0 < wrow0 + 31 - W;
+    if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk) || win) {
+      const int kmin = win ? row - W : -1;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int k0 = kv0 + acc_key(jj, half), k1 = k0 + 32;
-        sc[0][jj] = ((CAUSAL && k0 > row) || k0 >= nk) ? kNegInf : sc[0][jj];
-        sc[1][jj] = ((CAUSAL && k1 > row) || k1 >= nk) ? kNegInf : sc[1][jj];
+        sc[0][jj] = ((CAUSAL && k0 > row) || k0 >= nk || k0 < kmin) ? kNegInf : sc[0][jj];
+        sc[1][jj] = ((CAUSAL && k1 > row) || k1 >= nk || k1 < kmin) ? kNegInf : sc[1][jj];
       }
     }
     // A single wave issues an independent VALU op about every 5 cycles but a
@@ -751,7 +815,7 @@ void fwd_pp_kernel(const FwdParams p) {
       phase_begin(ph);
       if (r & 1) {                                  // S(j), j = (u - 1) / 2
         const int j = (u - 1) >> 1;
-        if (j < nt_w) softmax(j * BC);
+        if (j >= lo_w && j < nt_w) softmax((jbase + j) * BC);
       } else {                                      // G(j), j = u / 2 - 1
         const int j = (u >> 1) - 1;
         const int SK = (r / 2) % STAGES;            // stage of tile j + 1 (a constant once unrolled)
@@ -759,10 +823,10 @@ void fwd_pp_kernel(const FwdParams p) {
 #if FA_FWD_PRIO
         __builtin_amdgcn_s_setprio(1);
 #endif
-        if (j >= 0 && j + 1 < nt_w) gunit(SK, SV);
+        if (j >= lo_w && j + 1 < nt_w) gunit(SK, SV);
         else {
-          if (j + 1 < nt_w) scores(SK);
-          if (j >= 0 && j < nt_w) accumulate(SV);
+          if (j + 1 >= lo_w && j + 1 < nt_w) scores(SK);
+          if (j >= lo_w && j < nt_w) accumulate(SV);
         }
 #if FA_FWD_PRIO
         __builtin_amdgcn_s_setprio(0);
@@ -776,7 +840,7 @@ void fwd_pp_kernel(const FwdParams p) {
   if (row < nq) {
     const float l_o = lsum[0];
     const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
-    TOut* op = reinterpret_cast<TOut*>(p.o) + b * p.o_stride[0] + hq * p.o_stride[1] + (int64_t)row * p.o_stride[2];
+    TOut* op = reinterpret_cast<TOut*>(p.o) + sv.o + (int64_t)row * p.o_stride[2];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -794,7 +858,7 @@ void fwd_pp_kernel(const FwdParams p) {
       }
     if (p.lse != nullptr && half == 0) {
       const float lse = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
-      p.lse[((int64_t)b * p.heads_q + hq) * nq + row] = lse;
+      p.lse[sv.lse + row] = lse;
     }
   }
 }

@@ -18,6 +18,13 @@ struct FwdParams {
   int n_qtiles;
   float scale_log2;  // softmax scale * log2(e)
   bool causal, in_fp32, out_fp32;
+  // Packed batch (null: dense): sequence b owns tokens cu_seqlens[b] ..
+  // cu_seqlens[b+1]-1 of q, k, v and o; strides[2] is the token stride,
+  // strides[1] the head stride, strides[0] unused; seqlen_q = seqlen_k = the
+  // longest sequence; LSE is [heads_q, total].
+  const int32_t* cu_seqlens;
+  int total;
+  int window;        // sliding window (causal only): row r sees keys r-window .. r; -1 for none
 };
 
 struct DecodeParams {

@@ -130,16 +130,19 @@ def attention_ref(q, k, v, scale: float, causal: bool = False, q_positions=None,
     return O, L
 
 
-def varlen_ref(q, k, v, cu_seqlens, scale: float, causal: bool = False, window=None, rows=None):
+def varlen_ref(q, k, v, cu_seqlens, scale: float, causal: bool = False, window=None, rows=None, values=None):
     """Attention over packed sequences.
 
     q: [total, Hq, d]; k, v: [total, Hkv, d] (token-major, all sequences
     concatenated); cu_seqlens: [batch + 1] offsets, sequence b owning tokens
     cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k and v alike, with positions
     counted from its own start. ``rows`` optionally restricts the work to a
-    list of packed token indices (others stay O = 0, LSE = -inf).
+    list of packed token indices (others stay O = 0, LSE = -inf). ``values``
+    maps stored entries to numbers (for bfloat16 bit patterns), applied to the
+    slices a sequence uses.
     Returns O [total, Hq, dv] and LSE [Hq, total] in fp64.
     """
+    conv = values if values is not None else (lambda x: x)
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     total, Hq, d = q.shape
     cu = [int(x) for x in cu_seqlens]
@@ -153,9 +156,9 @@ def varlen_ref(q, k, v, cu_seqlens, scale: float, causal: bool = False, window=N
         local = np.arange(s1 - s0) if want is None else np.array([r - s0 for r in range(s0, s1) if r in want])
         if local.size == 0:
             continue
-        qb = _as64(q[s0 + local]).transpose(1, 0, 2)[None]         # [1, Hq, n_rows, d]
-        kb = _as64(k[s0:s1]).transpose(1, 0, 2)[None]
-        vb = _as64(v[s0:s1]).transpose(1, 0, 2)[None]
+        qb = _as64(conv(q[s0 + local])).transpose(1, 0, 2)[None]   # [1, Hq, n_rows, d]
+        kb = _as64(conv(k[s0:s1])).transpose(1, 0, 2)[None]
+        vb = _as64(conv(v[s0:s1])).transpose(1, 0, 2)[None]
         ob, lb = attention_ref(qb, kb, vb, scale, causal=causal, q_positions=local, window=window)
         O[s0 + local] = ob[0].transpose(1, 0, 2)
         L[:, s0 + local] = lb[0]

@@ -79,6 +79,41 @@ def test_fwd_rejects_before_launch(kw, status, needle):
     assert needle in msg
 
 
+def _varlen(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=None, cu=FAKE + 0x400000,
+             B=2, Hq=4, Hkv=2, T=100, maxl=64, d=128, qs=(512, 128), ks=(256, 128), vs=(256, 128), os_=(512, 128),
+             outd=0, mask=1, win=-1, scale=0.125)
+    a.update(kw)
+    arr = lambda t: (ctypes.c_int64 * 2)(*t) if t is not None else None
+    st = lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["Hq"], a["Hkv"], a["T"],
+                           a["maxl"], a["d"], arr(a["qs"]), arr(a["ks"]), arr(a["vs"]), arr(a["os_"]), a["outd"],
+                           a["mask"], a["win"], a["scale"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cu=None), 1, "non-null"),
+    (dict(os_=None), 1, "stride"),
+    (dict(T=0), 1, "positive"),
+    (dict(maxl=0), 1, "positive"),
+    (dict(win=-2), 1, "window"),
+    (dict(mask=3), 1, "mask"),
+    (dict(scale=-1.0), 1, "softmax_scale"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(Hq=6, Hkv=4), 2, "multiple"),
+    (dict(mask=0, win=16), 2, "causal"),
+    (dict(o=FAKE + 0x300008), 2, "aligned"),
+    (dict(qs=(516, 128)), 2, "16 bytes"),
+    (dict(ks=((1 << 24) + 8, 128)), 2, "token strides"),
+    (dict(o=FAKE + 0x10), 1, "overlaps"),
+])
+def test_fwd_varlen_rejects_before_launch(kw, status, needle):
+    st, msg = _varlen(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def _dec(**kw):
     lib = _lib.load()
     a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lens=FAKE + 0x300000, o=FAKE + 0x400000, lse=None,
