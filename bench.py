@@ -7,9 +7,12 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
      kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
      and merge kernel).
-After the timed steps, the same decode is timed again against a paged cache
-(fa_decode_paged: 16-token pages in a token-major pool, shuffled block table)
-and reported as ``decode_paged``; it is not part of the step.
+After the timed steps, three more paths are timed on their own (not part of
+the step): the same decode against a paged cache (fa_decode_paged: 16-token
+pages in a token-major pool, shuffled block table) as ``decode_paged``, and
+through fa_fwd_varlen the 8192-token sliding-window-1024 prefill
+(``prefill_window``) and a packed batch of 16 causal sequences of 1..8192
+tokens (``prefill_varlen``).
 Inputs are generated and uploaded before the timed region. W untimed warmup
 steps, then exactly K timed steps between two device synchronisations. Kernel
 durations come from HIP events recorded on the stream the kernels run on.
@@ -150,6 +153,45 @@ def run(args):
         pev[i][1].record(stream)
     torch.cuda.synchronize()
     pag_ms = [e[0].elapsed_time(e[1]) for e in pev]
+    del pk_d, pv_d
+
+    def time_launches(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+
+    # packed prefill: sliding window and mixed lengths, each timed on its own
+    extra = {}
+    for key, name in (("prefill_window", "c7_window_8k"), ("prefill_varlen", "c6_varlen_causal")):
+        vc = W.VARLEN_CONFIGS[name]
+        vl = W.varlen_lengths(vc)
+        vq, vk, vv, vcu = W.make_varlen_inputs(vc.heads_q, vc.heads_kv, vc.head_dim, vl, seed=vc.seed)
+        vq, vk, vv = to_dev(vq), to_dev(vk), to_dev(vv)
+        vcu = torch.from_numpy(vcu).to(dev)
+        vo = torch.empty_like(vq)
+        vlse = torch.empty(vc.heads_q, int(vl.sum()), dtype=torch.float32, device=dev)
+        win = vc.window if vc.window >= 0 else None
+        ms = time_launches(lambda: fa.fwd_varlen(vq, vk, vv, vcu, int(vl.max()), causal=vc.causal, window=win,
+                                                 scale=vc.scale, out=vo, lse=vlse))
+        if win is not None:
+            fl = sum(cm.window_flops(vc.heads_q, int(n), vc.head_dim, win) for n in vl)
+        else:
+            fl = cm.varlen_flops(vl, vc.heads_q, vc.head_dim, vc.causal)
+        tf = fl / (ms * 1e-3) / 1e12
+        extra[key] = {"ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_launch": fl,
+                      "workload": f"{vc.n_seqs} sequence(s), lengths {int(vl.min())}..{int(vl.max())} "
+                                  f"(total {int(vl.sum())}), Hq{vc.heads_q} Hkv{vc.heads_kv} d{vc.head_dim}, "
+                                  + (f"causal window {win}" if win is not None else "causal"),
+                      "kernel": "fa_fwd_varlen"}
+        del vq, vk, vv, vo
 
     pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
     kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
@@ -196,6 +238,7 @@ def run(args):
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_dec,
                             "kernel": "fa_decode (split + merge)"},
+        **extra,
         "kernel_sources": sources_hash(),
     }
     if not args.no_cpu_baseline:
@@ -332,7 +375,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-trace", metavar="DIR")

@@ -30,6 +30,23 @@ def attention_flops(batch: int, heads_q: int, seqlen_q: int, seqlen_k: int, head
     return f / 2.0 if causal else f
 
 
+def window_flops(heads_q: int, seqlen: int, head_dim: int, window: int) -> float:
+    """Algorithmic FLOPs of one sequence under a sliding window W on top of the
+    causal mask: 4 * d per visible (row, key) pair, counted exactly (row r sees
+    min(r, W) + 1 keys), since the halved-square convention of the plain
+    causal mask has no analogue for a band."""
+    n, w = int(seqlen), int(window)
+    full = max(0, n - w)                       # rows r >= W see W + 1 keys
+    ramp = min(n, w)                           # rows r < W see r + 1 keys
+    pairs = full * (w + 1) + ramp * (ramp + 1) // 2
+    return 4.0 * heads_q * head_dim * pairs
+
+
+def varlen_flops(lengths: Iterable[int], heads_q: int, head_dim: int, causal: bool) -> float:
+    """Sum over packed sequences of attention_flops(1, Hq, L, L, d, causal)."""
+    return sum(attention_flops(1, heads_q, int(n), int(n), head_dim, causal) for n in lengths)
+
+
 def causal_kv_tiles(i: int, Br: int, Bc: int, seqlen: int) -> int:
     """Number of K/V tiles query tile i (0-based) loads under the causal skip bound.
 

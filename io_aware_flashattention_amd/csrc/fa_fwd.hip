@@ -136,6 +136,40 @@ __device__ __forceinline__ SeqView seq_view(const FwdParams& p, int b, int hq, i
   return s;
 }
 
+// Logical work item (batch, kv head, query tile, query head of the group;
+// head fastest) of hardware workgroup wg, or -1 for grid padding. Workgroups
+// are dealt to the 8 XCDs round-robin (wg % 8), each XCD with its own L2.
+//   Dense batch: every (batch, kv head) row of query tiles costs the same, so
+//   each XCD takes a contiguous range of the logical order; its resident
+//   workgroups then share one kv head's K/V in its L2.
+//   Packed batch: rows cost what their sequence's length makes them cost, and
+//   contiguous ranges would leave some XCDs with long sequences and others
+//   idle. Chunks of G workgroups (the query heads that share a kv head and a
+//   query tile, kept on one XCD) are dealt to the XCDs in a snake order: 0..7,
+//   7..0, 0..7, ... Along one row, XCD x then gets tiles x, 15-x, 16+x, 31-x,
+//   ..., whose causal costs pair up heavy with light, and the XCDs stay
+//   balanced whatever the length mix. The grid is padded to whole rounds.
+__device__ __forceinline__ int work_item(int wg, int n, const FwdParams& p) {
+  if (p.cu_seqlens != nullptr) {
+    const int G = p.group;
+    const int x = wg & 7, k = wg >> 3;
+    const int r = k / G, g = k - r * G;
+    const int j = (r & 1) ? 7 - x : x;
+    const int L = (8 * r + j) * G + g;
+    return L < p.n_items ? L : -1;
+  }
+  const int xcd = wg & 7, slot = wg >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Grid for the logical work items of a launch.
+inline int64_t grid_for(const FwdParams& p) {
+  if (p.cu_seqlens == nullptr) return p.n_items;
+  const int64_t chunks = p.n_items / p.group;
+  return (chunks + 7) / 8 * 8 * p.group;
+}
+
 }  // namespace
 
 namespace detail {
@@ -163,11 +197,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 
   // ---- which (batch, head, query tile): XCD-aware, heavy causal tiles first,
   // the query heads of one kv head next to each other
-  const int n = gridDim.x;
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7, slot = wg >> 3;
-  const int per = n >> 3, rem = n & 7;
-  int L = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  int L = work_item(blockIdx.x, gridDim.x, p);
+  if (L < 0) return;                         // padding of the last XCD round (whole workgroup)
   const int g = L % p.group;
   L /= p.group;
   const int t = L % p.n_qtiles;
@@ -521,11 +552,8 @@ void fwd_pp_kernel(const FwdParams p) {
   }
 #endif
 
-  const int n = gridDim.x;
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7, slot = wg >> 3;
-  const int per = n >> 3, rem = n & 7;
-  int L = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  int L = work_item(blockIdx.x, gridDim.x, p);
+  if (L < 0) return;                         // padding of the last XCD round (whole workgroup)
   const int g = L % p.group;
   L /= p.group;
   const int t = L % p.n_qtiles;
@@ -873,7 +901,8 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr int BRW = 32 * R * NW;
   FwdParams q = p;
   q.n_qtiles = (p.seqlen_q + BRW - 1) / BRW;
-  const int64_t wgs = (int64_t)q.batch * q.heads_q * q.n_qtiles;
+  q.n_items = q.batch * q.heads_q * q.n_qtiles;
+  const int64_t wgs = grid_for(q);
   hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, R, STAGES>), dim3((unsigned)wgs), dim3(NW * 64),
                      0, stream, q);
   return hipGetLastError();
@@ -883,7 +912,8 @@ template <int D, bool CAUSAL, typename TOut, int STAGES>
 hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
   q.n_qtiles = (p.seqlen_q + 255) / 256;
-  const int64_t wgs = (int64_t)q.batch * q.heads_q * q.n_qtiles;
+  q.n_items = q.batch * q.heads_q * q.n_qtiles;
+  const int64_t wgs = grid_for(q);
   hipLaunchKernelGGL((detail::fwd_pp_kernel<D, CAUSAL, TOut, STAGES>), dim3((unsigned)wgs), dim3(512), 0, stream, q);
   return hipGetLastError();
 }

@@ -16,6 +16,7 @@ struct FwdParams {
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
   int batch, heads_q, heads_kv, group, seqlen_q, seqlen_k, head_dim;
   int n_qtiles;
+  int n_items;       // batch * heads_q * n_qtiles logical workgroups
   float scale_log2;  // softmax scale * log2(e)
   bool causal, in_fp32, out_fp32;
   // Packed batch (null: dense): sequence b owns tokens cu_seqlens[b] ..

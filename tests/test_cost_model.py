@@ -63,3 +63,16 @@ def test_compulsory_bytes_long_context_gqa():
     # causal GQA prefill B1 Hq64 Hkv8 N8192 d128 bf16: Q + K + V + O + LSE
     b = cm.compulsory_bytes(1, 64, 8, 8192, 128)
     assert b == 134217728 + 2 * 16777216 + 134217728 + 4 * 64 * 8192
+
+
+def test_window_flops_counts_visible_pairs():
+    for n, w in [(1, 0), (5, 0), (5, 2), (10, 3), (10, 20), (64, 63)]:
+        pairs = sum(1 for r in range(n) for c in range(n) if c <= r and r - c <= w)
+        assert cm.window_flops(3, n, 8, w) == 4.0 * 3 * 8 * pairs
+    # the pages' example: 8192 tokens, keys at most 1024 behind
+    assert cm.window_flops(1, 8192, 1, 1024) == 4.0 * (7168 * 1025 + 1024 * 1025 // 2)
+
+
+def test_varlen_flops_sums_sequences():
+    assert cm.varlen_flops([3, 0, 5], 2, 4, False) == 4.0 * 2 * 4 * (9 + 25)
+    assert cm.varlen_flops([3, 5], 2, 4, True) == 4.0 * 2 * 4 * (9 + 25) / 2
