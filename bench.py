@@ -25,8 +25,9 @@ MI355X peaks; ``cpu_baseline`` times the fp64 oracle on a sample of the same
 prefill workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-    python bench.py --summarize-trace DIR --out FILE     (rocprofv3 kernel stats -> text)
-    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE  (HBM traffic per launch)
+    python bench.py --summarize-trace DIR --out FILE [--steps K --warmup W]   (rocprofv3 kernel trace -> text)
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE [--steps K --warmup W]  (HBM bytes per launch)
+  (--steps/--warmup: those of the profiled run, so its dispatches can be split into the bench's phases)
 """
 from __future__ import annotations
 
@@ -143,7 +144,7 @@ def run(args):
     def paged():
         fa.decode_paged(dq_d, pk_d, pv_d, ptab_d, lens_d, scale=dc.scale, out=do, lse=dlse, workspace=ws)
 
-    for _ in range(max(1, args.warmup)):
+    for _ in range(args.warmup):
         paged()
     pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -156,7 +157,7 @@ def run(args):
     del pk_d, pv_d
 
     def time_launches(fn):
-        for _ in range(max(1, args.warmup)):
+        for _ in range(args.warmup):
             fn()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -300,16 +301,61 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(d: str, out: str, cmd: str):
-    """rocprofv3 --kernel-trace --stats output directory -> short text table."""
+def _dispatch_labels(rows, name_key: str, n_launch: int):
+    """Label per-dispatch rows (sorted by Dispatch_Id) with the bench phase
+    they belong to. The bench launches, in this order: n_launch steps of
+    (prefill, decode split, decode merge); n_launch paged decodes (paged split,
+    merge); n_launch window prefills; n_launch packed prefills. The prefill
+    kernel is the same instantiation for the last three, so the phase comes
+    from the dispatch order."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    seen = {"fwd": 0, "merge": 0}
+    out = []
+    for r in rows:
+        name = r.get(name_key, "")
+        if re.search(r"fwd_\w*kernel", name):
+            i = seen["fwd"]
+            seen["fwd"] += 1
+            label = ("prefill c4a (step)", "prefill window c7", "prefill varlen c6")[min(2, i // n_launch)]
+        elif "decode_split" in name:            # contiguous: template flag false (mangled "Lb0E")
+            label = "decode split (step)" if ("Lb0E" in name or "false" in name) else "paged decode split"
+        elif "decode_merge" in name:
+            i = seen["merge"]
+            seen["merge"] += 1
+            label = "decode merge (step)" if i < n_launch else "paged decode merge"
+        else:
+            label = None
+        out.append((label, r))
+    return out
+
+
+def summarize_trace(d: str, out: str, cmd: str, n_launch: int, n_timed: int):
+    """rocprofv3 --kernel-trace --stats output directory -> short text tables:
+    per bench phase from the per-dispatch trace, then rocprofv3's own stats."""
     stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
-    if not stats:
-        sys.exit(f"no kernel_stats.csv under {d}")
-    rows = _read_csv(stats[0])
+    trace = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not stats or not trace:
+        sys.exit(f"no kernel_stats.csv / kernel_trace.csv under {d}")
     lines = [f"# rocprofv3 kernel statistics", "", f"command: `{cmd}`", "",
              f"kernel sources: {sources_hash()}", "",
-             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
-    for r in rows:
+             f"Per bench phase (per-dispatch trace; {n_launch} launches per phase: the warm-up, then the "
+             f"{n_timed} timed ones):", "",
+             f"| phase | kernel | dispatches | avg us (all) | avg us (last {n_timed}) | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    groups = {}
+    for label, r in _dispatch_labels(_read_csv(trace[0]), "Kernel_Name", n_launch):
+        if label is None:
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((label, r["Kernel_Name"]), []).append(dur)
+    for (label, name), ds in groups.items():
+        short = name if len(name) < 70 else name[:67] + "..."
+        tail = ds[-n_timed:]
+        lines.append(f"| {label} | `{short}` | {len(ds)} | {sum(ds) / len(ds):.2f} | {sum(tail) / len(tail):.2f} | "
+                     f"{min(ds):.2f} | {max(ds):.2f} |")
+    lines += ["", "rocprofv3 --stats (per kernel name; the prefill kernel's row mixes its three phases):", "",
+              "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in _read_csv(stats[0]):
         name = r.get("Name", "")
         short = name if len(name) < 90 else name[:87] + "..."
         avg = float(r.get("AverageNs", 0)) / 1e3
@@ -320,51 +366,42 @@ def summarize_trace(d: str, out: str, cmd: str):
     print("\n".join(lines))
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_write: str):
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_write: str, n_launch: int):
     """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench -> HBM
-    bytes per launch of each kernel, scaled by what the counters read for the
-    calibration copy of known size."""
-    def per_kernel(dd, counter):
+    bytes per launch of each kernel of the step, scaled by what the counters
+    read for the calibration copy of known size."""
+    def per_phase(dd, counter):
         files = sorted(glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True))
         if not files:
             sys.exit(f"no counter_collection.csv under {dd}")
-        acc = {}
-        for r in _read_csv(files[0]):
-            if r.get("Counter_Name") != counter:
-                continue
-            name = r.get("Kernel_Name", "")
-            acc.setdefault(name, []).append(float(r.get("Counter_Value", 0)) * 1024.0)   # KiB -> bytes
-        return acc
+        rows = [r for r in _read_csv(files[0]) if r.get("Counter_Name") == counter]
+        acc, copy = {}, []
+        for label, r in _dispatch_labels(rows, "Kernel_Name", n_launch):
+            v = float(r.get("Counter_Value", 0)) * 1024.0          # KiB -> bytes
+            if label is not None:
+                acc.setdefault(label, []).append(v)
+            elif "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower():
+                copy.append(v)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, (max(copy) if copy else None)
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
-
-    def pick(acc, pred):
-        vals = [v for n, vs in acc.items() if pred(n) for v in vs]
-        return sum(vals) / len(vals) if vals else None
-
-    is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
-    copy_fetch = max((max(vs) for n, vs in fetch.items() if is_copy(n)), default=None)
-    copy_write = max((max(vs) for n, vs in write.items() if is_copy(n)), default=None)
+    fetch, copy_fetch = per_phase(fetch_dir, "FETCH_SIZE")
+    write, copy_write = per_phase(write_dir, "WRITE_SIZE")
     sf = COPY_BYTES / copy_fetch if copy_fetch else 1.0
     sw = COPY_BYTES / copy_write if copy_write else 1.0
-    is_fwd = lambda n: re.search(r"fwd_\w*kernel", n) is not None
-    pre_f = pick(fetch, is_fwd)
-    pre_w = pick(write, is_fwd)
-    # contiguous decode only: the paged instantiation of the split kernel is told apart by its template flag;
-    # the merge kernel is shared, so its per-launch average covers both
-    is_split = lambda n: "decode_split" in n and "true" not in n
-    dec_f = (pick(fetch, is_split) or 0) + (pick(fetch, lambda n: "decode_merge" in n) or 0)
-    dec_w = (pick(write, is_split) or 0) + (pick(write, lambda n: "decode_merge" in n) or 0)
+    g = lambda acc, k: acc.get(k, 0.0)
     d = {
         "kernel_sources": sources_hash(),
         "command_fetch": cmd_fetch, "command_write": cmd_write,
         "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter_bytes": copy_fetch, "write_counter_bytes": copy_write,
                              "fetch_scale": sf, "write_scale": sw},
-        "prefill_fetch_bytes": pre_f * sf if pre_f else None, "prefill_write_bytes": pre_w * sw if pre_w else None,
-        "decode_fetch_bytes": dec_f * sf, "decode_write_bytes": dec_w * sw,
+        "per_phase_bytes": {k: {"fetch": g(fetch, k) * sf, "write": g(write, k) * sw}
+                            for k in sorted(set(fetch) | set(write))},
+        "prefill_fetch_bytes": g(fetch, "prefill c4a (step)") * sf,
+        "prefill_write_bytes": g(write, "prefill c4a (step)") * sw,
+        "decode_fetch_bytes": (g(fetch, "decode split (step)") + g(fetch, "decode merge (step)")) * sf,
+        "decode_write_bytes": (g(write, "decode split (step)") + g(write, "decode merge (step)")) * sw,
     }
-    d["prefill_bytes_per_launch"] = (d["prefill_fetch_bytes"] or 0) + (d["prefill_write_bytes"] or 0)
+    d["prefill_bytes_per_launch"] = d["prefill_fetch_bytes"] + d["prefill_write_bytes"]
     d["decode_bytes_per_launch"] = d["decode_fetch_bytes"] + d["decode_write_bytes"]
     with open(out, "w") as f:
         json.dump(d, f, indent=2)
@@ -383,11 +420,12 @@ def main():
     ap.add_argument("--cmd", nargs="*", default=[], help="commands recorded in a summary")
     ap.add_argument("--out")
     args = ap.parse_args()
+    n_launch = args.warmup + args.steps       # launches per bench phase of the profiled run
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace, args.out, " ".join(args.cmd))
+        return summarize_trace(args.summarize_trace, args.out, " ".join(args.cmd), n_launch, args.steps)
     if args.summarize_pmc:
         cmds = args.cmd + ["", ""]
-        return summarize_pmc(*args.summarize_pmc, args.out, cmds[0], cmds[1])
+        return summarize_pmc(*args.summarize_pmc, args.out, cmds[0], cmds[1], n_launch)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         sys.exit("bench.py measures one GPU (--gpus 1): the attention path runs on a single MI355X "
