@@ -3,10 +3,10 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package. The product path never does.
 """
-from .attention import (attention_ref, block_summary, decode_ref, merge_lse,
+from .attention import (attention_bwd_ref, attention_ref, block_summary, decode_ref, merge_lse,
                         merge_summaries, paged_decode_ref, paged_rows, split_decode_ref,
                         stream_attention, varlen_ref)
 
-__all__ = ["attention_ref", "stream_attention", "block_summary", "merge_summaries",
+__all__ = ["attention_ref", "attention_bwd_ref", "stream_attention", "block_summary", "merge_summaries",
            "merge_lse", "decode_ref", "split_decode_ref", "paged_rows", "paged_decode_ref",
            "varlen_ref"]

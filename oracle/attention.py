@@ -39,6 +39,13 @@ What it computes, and where the pages define it:
   the token axis with cumulative offsets cu_seqlens, each attending only to
   itself ("FlashAttention Explained", section "Trade-offs, Gotchas, and What
   Goes Wrong": varlen kernels skip pad tokens given cumulative lengths).
+* ``attention_bwd_ref`` -- gradients of the forward pass for an incoming dO:
+  dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+  dQ = scale dS K, dK = scale dS^T Q, with P recomputed from the scores
+  ("FlashAttention Explained", section "Backward Pass: Recomputation Beats
+  Storage"; "How FlashAttention Reduces HBM Traffic Exactly", section
+  "Training: recomputation replaces saved attention probabilities"). Under
+  GQA a kv head's dK and dV sum the contributions of its query heads.
 * ``decode_ref`` -- single-token decode: the same attention for one query row
   per head over the first L_b cached keys of each sequence.
 * ``paged_rows`` / ``paged_decode_ref`` -- the same decode over a paged cache:
@@ -128,6 +135,43 @@ def attention_ref(q, k, v, scale: float, causal: bool = False, q_positions=None,
                 live = l > 0
                 L[b, h, r0:r1][live] = m[live] + np.log(l[live])
     return O, L
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool = False, window=None, row_block: int = _ROW_BLOCK):
+    """Gradients of attention_ref's O with respect to q, k and v, given dO.
+
+    q, do: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. Returns dQ, dK, dV (shapes of
+    q, k, v) and D = rowsum(dO * O) [B, Hq, N], all fp64. P is recomputed per
+    block of rows from the scores and the row statistics, never stored whole.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O, _ = attention_ref(q, k, v, scale, causal=causal, window=window, row_block=row_block)
+    D = (do * O).sum(axis=3)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows, cols = np.arange(Nq), np.arange(Nk)
+    for b in range(B):
+        for h in range(Hq):
+            K, V = k[b, h // G], v[b, h // G]
+            for r0 in range(0, Nq, row_block):
+                r1 = min(Nq, r0 + row_block)
+                S = scale * (q[b, h, r0:r1] @ K.T)
+                if causal:
+                    S[cols[None, :] > rows[r0:r1, None]] = -np.inf
+                if window is not None:
+                    S[cols[None, :] < rows[r0:r1, None] - window] = -np.inf
+                P, _, _ = _softmax_rows(S)
+                dO = do[b, h, r0:r1]
+                dv[b, h // G] += P.T @ dO
+                dP = dO @ V.T
+                dS = P * (dP - D[b, h, r0:r1, None])
+                dq[b, h, r0:r1] = scale * (dS @ K)
+                dk[b, h // G] += scale * (dS.T @ q[b, h, r0:r1])
+    return dq, dk, dv, D
 
 
 def varlen_ref(q, k, v, cu_seqlens, scale: float, causal: bool = False, window=None, rows=None, values=None):

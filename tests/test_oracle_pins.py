@@ -9,7 +9,7 @@ import scipy.special
 from hypothesis import given, settings
 from hypothesis import strategies as st
 
-from oracle import (attention_ref, block_summary, decode_ref, merge_lse, merge_summaries,
+from oracle import (attention_bwd_ref, attention_ref, block_summary, decode_ref, merge_lse, merge_summaries,
                     paged_decode_ref, paged_rows, split_decode_ref, stream_attention, varlen_ref)
 from tests.conftest import golden
 
@@ -554,3 +554,71 @@ def test_varlen_single_sequence_is_dense_and_rows_subset():
     assert np.array_equal(Os[rows], O[rows]) and np.array_equal(Ls[:, rows], L[:, rows])
     others = [r for r in range(33) if r not in rows]
     assert np.all(Os[others] == 0) and np.all(np.isneginf(Ls[:, others]))
+
+
+# ---------------------------------------------------------------- backward --
+
+def _loss_grad_fd(q, k, v, w, scale, causal, window, which, idx, eps=1e-6):
+    """Central difference of L = sum(O * w) with respect to one input entry."""
+    args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    vals = []
+    for sgn in (1, -1):
+        a = {n: x.copy() for n, x in args.items()}
+        a[which][idx] += sgn * eps
+        O, _ = attention_ref(a["q"], a["k"], a["v"], scale, causal=causal, window=window)
+        vals.append(float((O * w).sum()))
+    return (vals[0] - vals[1]) / (2 * eps)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 2)])
+def test_backward_matches_finite_differences(causal, window):
+    rng = np.random.default_rng(81)
+    B, Hq, Hkv, N, d, scale = 1, 4, 2, 7, 3, 0.7
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    w = rng.standard_normal((B, Hq, N, d))                  # dO = dL/dO for L = sum(O * w)
+    dq, dk, dv, _ = attention_bwd_ref(q, k, v, w, scale, causal=causal, window=window)
+    for which, grad, shape in (("q", dq, q.shape), ("k", dk, k.shape), ("v", dv, v.shape)):
+        for flat in rng.choice(int(np.prod(shape)), size=12, replace=False):
+            idx = np.unravel_index(int(flat), shape)
+            fd = _loss_grad_fd(q, k, v, w, scale, causal, window, which, idx)
+            assert abs(fd - grad[idx]) < 1e-7, (which, idx, fd, grad[idx])
+
+
+def test_backward_matches_torch_autograd_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(82)
+    B, Hq, Hkv, N, d, scale = 2, 4, 2, 9, 5, 0.45
+    q, do = rng.standard_normal((B, Hq, N, d)), rng.standard_normal((B, Hq, N, d))
+    k, v = rng.standard_normal((B, Hkv, N, d)), rng.standard_normal((B, Hkv, N, d))
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+        vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+        s = scale * torch.matmul(tq, kk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+        o = torch.matmul(torch.softmax(s, dim=-1), vv)
+        o.backward(torch.tensor(do))
+        dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal=causal)
+        assert np.abs(dq - tq.grad.numpy()).max() < 1e-12
+        assert np.abs(dk - tk.grad.numpy()).max() < 1e-12
+        assert np.abs(dv - tv.grad.numpy()).max() < 1e-12
+
+
+def test_backward_row_term_identity_and_invariants():
+    """D is rowsum(dO * O); softmax ignores a shift added to every key, so the
+    key gradients sum to zero; with dO = 1 each row of P sums to one, so the
+    value gradients sum to the number of rows."""
+    rng = np.random.default_rng(83)
+    B, H, N, d, scale = 1, 2, 11, 4, 0.6
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    dq, dk, dv, D = attention_bwd_ref(q, k, v, do, scale, causal=True)
+    O, _ = attention_ref(q, k, v, scale, causal=True)
+    assert np.abs(D - (do * O).sum(axis=3)).max() < 1e-13
+    # softmax is invariant to adding the same vector to every key: sum_j dK_j = 0
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+    # dV sums P^T dO: with dO = 1 everywhere, every row of P sums to one, so sum_j dV_j = N per column
+    _, _, dv1, _ = attention_bwd_ref(q, k, v, np.ones_like(do), scale, causal=True)
+    assert np.abs(dv1.sum(axis=2) - N).max() < 1e-12
