@@ -18,6 +18,9 @@
  *   fa_fwd_varlen  the same over packed variable-length sequences, with an
  *              optional sliding-window mask.
  *
+ *   fa_bwd     gradients of fa_fwd with respect to q, k and v, recomputing the
+ *              probabilities from the saved log-sum-exp.
+ *
  *   fa_decode  single-token decode against a KV cache, with the key axis split
  *              across workgroups; every split writes a partial output and its
  *              log-sum-exp, and a second small kernel merges the partials
@@ -228,6 +231,46 @@ FA_API fa_status_t fa_decode_paged(const void* q, const void* k_pages, const voi
                             int32_t num_pages, int32_t page_size, int32_t max_blocks_per_seq,
                             const int64_t page_stride[3], fa_dtype_t out_dtype, float softmax_scale,
                             int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs: one float per query
+ * row (rowsum(dO * O)). 0 for non-positive sizes.
+ */
+FA_API size_t fa_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seqlen_q);
+
+/*
+ * fa_bwd -- gradients of fa_fwd with respect to q, k and v, by recomputation:
+ * the probabilities are rebuilt tile by tile from q, k and the forward pass's
+ * log-sum-exp instead of being stored ("FlashAttention Explained: IO-Aware
+ * Attention, Tiling, Online Softmax and FP8 on Hopper", section "Backward
+ * Pass: Recomputation Beats Storage"). With P = exp(scale q k^T - lse) under
+ * the mask: D = rowsum(dout * o), dv = P^T dout, dP = dout v^T,
+ * dS = P * (dP - D), dq = scale dS k, dk = scale dS^T q. Under GQA dk and dv
+ * of a kv head sum the contributions of its query heads. No atomics: the
+ * result is deterministic.
+ *
+ * q, o, dout  [batch, heads_q, seqlen_q, head_dim] bf16, strides q_stride = {b, h, n}
+ * k, v        [batch, heads_kv, seqlen_k, head_dim] bf16, strides kv_stride
+ * lse         [batch, heads_q, seqlen_q] float32, contiguous, as fa_fwd wrote it
+ *             (with the same q, k, v, mask and softmax_scale; o is fa_fwd's output)
+ * dq          [batch, heads_q, seqlen_q, head_dim] grad_dtype, strides dq_stride
+ * dk, dv      [batch, heads_kv, seqlen_k, head_dim] grad_dtype, strides dkv_stride
+ * grad_dtype  BF16 (rounded once, nearest-even) or FP32
+ * mask        FA_MASK_NONE, or FA_MASK_CAUSAL (seqlen_q == seqlen_k)
+ * workspace   at least fa_bwd_workspace_bytes(batch, heads_q, seqlen_q) bytes,
+ *             16-byte aligned
+ *
+ * Supported: head_dim 64 or 128; heads_q % heads_kv == 0; 16-byte aligned
+ * pointers; input strides multiples of 8 elements, gradient strides multiples
+ * of 16 bytes. Otherwise FA_ERR_UNSUPPORTED. Gradients must not overlap any
+ * input, each other or the workspace (FA_ERR_INVALID_ARGUMENT).
+ */
+FA_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
+                          int32_t heads_kv, int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                          const int64_t q_stride[3], const int64_t kv_stride[3], const int64_t dq_stride[3],
+                          const int64_t dkv_stride[3], fa_dtype_t grad_dtype, fa_mask_t mask, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. Never NULL. */
 FA_API const char* fa_status_string(fa_status_t status);

@@ -21,8 +21,8 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
-            "fa_status_string", "fa_last_error_message")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd_workspace_bytes", "fa_bwd", "fa_decode_workspace_bytes",
+            "fa_decode", "fa_decode_paged", "fa_status_string", "fa_last_error_message")
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
 _lib = None
@@ -51,6 +51,13 @@ def load():
                                   _i32, _i32, _i32, _i32, _i32, _i32,       # batch, Hq, Hkv, total, max_seqlen, d
                                   _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, _i32,
                                   ctypes.c_float, _vp]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_bytes.argtypes = [_i32, _i32, _i32]                 # batch, heads_q, seqlen_q
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,     # q k v o dout lse dq dk dv
+                           _i32, _i32, _i32, _i32, _i32, _i32,              # batch Hq Hkv Nq Nk d
+                           _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                           _vp, ctypes.c_size_t, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
     lib.fa_decode.restype = ctypes.c_int
@@ -165,6 +172,44 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
                            float(scale), _stream(q.device))
     _check(st)
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+        lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+        grad_dtype: torch.dtype | None = None, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Backward of ``fwd``. q, o, dout [B,Hq,N,d] bf16 sharing strides; k, v [B,Hkv,Nk,d] bf16
+    sharing strides; lse float32 [B,Hq,N] from ``fwd``. Returns (dq, dk, dv)."""
+    lib = load()
+    B, Hq, N, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v, o and dout must be bfloat16")
+    if o.stride() != q.stride() or dout.stride() != q.stride() or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must share q's shape and strides")
+    if v.stride() != k.stride() or v.shape != k.shape:
+        raise ValueError("v must share k's shape and strides")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gdt = grad_dtype or torch.bfloat16
+    dq = torch.empty((B, Hq, N, d), dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty((B, Hkv, Nk, d), dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty((B, Hkv, Nk, d), dtype=gdt, device=q.device) if dv is None else dv
+    if dk.stride() != dv.stride() or dk.dtype != dv.dtype or dq.dtype != dk.dtype:
+        raise ValueError("dk and dv must share strides, and all gradients one dtype")
+    need = int(lib.fa_bwd_workspace_bytes(B, Hq, N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, Nk, d, _strides3(q), _strides3(k),
+                    _strides3(dq), _strides3(dk), _dtype_code(dq.dtype),
+                    FA_MASK_CAUSAL if causal else FA_MASK_NONE, float(scale), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st)
+    return dq, dk, dv
 
 
 def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seqlen: int, head_dim: int) -> int:

@@ -16,7 +16,7 @@ OBJ = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 # Packed-FP32 VALU forms are kept out of every device object.
@@ -24,7 +24,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 # The attention kernels never produce or test NaN (masked scores are -inf and
 # infinities stay honoured), so max() needs no NaN-quieting of its inputs.
-PER_SOURCE = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
+PER_SOURCE = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"],
+              "fa_bwd.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -109,6 +109,94 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
   return ok();
 }
 
+size_t fa_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
+  if (batch <= 0 || heads_q <= 0 || seqlen_q <= 0) return 0;
+  return (size_t)batch * heads_q * seqlen_q * sizeof(float);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                   int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[3],
+                   const int64_t kv_stride[3], const int64_t dq_stride[3], const int64_t dkv_stride[3],
+                   fa_dtype_t grad_dtype, fa_mask_t mask, float softmax_scale, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: tensor pointers must be non-null");
+  if (!q_stride || !kv_stride || !dq_stride || !dkv_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: stride arrays must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: sizes must be positive");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: softmax_scale must be finite and positive (got %g)",
+                (double)softmax_scale);
+  if (grad_dtype != FA_DTYPE_BF16 && grad_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: unknown grad_dtype %d", (int)grad_dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: unknown mask %d", (int)mask);
+  for (int i = 0; i < 3; ++i)
+    if (q_stride[i] < 0 || kv_stride[i] < 0 || dq_stride[i] < 0 || dkv_stride[i] < 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: strides must be non-negative");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: head_dim %d not supported (64 or 128)", head_dim);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+  if (mask == FA_MASK_CAUSAL && seqlen_q != seqlen_k)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: causal mask needs seqlen_q == seqlen_k (got %d, %d)", seqlen_q, seqlen_k);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || !aligned16(lse))
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: pointers must be 16-byte aligned");
+  const int gvec = grad_dtype == FA_DTYPE_BF16 ? 8 : 4;
+  for (int i = 0; i < 3; ++i) {
+    if (q_stride[i] % 8 || kv_stride[i] % 8)
+      return fail(FA_ERR_UNSUPPORTED, "fa_bwd: input strides must be multiples of 8 elements");
+    if (dq_stride[i] % gvec || dkv_stride[i] % gvec)
+      return fail(FA_ERR_UNSUPPORTED, "fa_bwd: gradient strides must be multiples of %d elements", gvec);
+  }
+  const size_t need = fa_bwd_workspace_bytes(batch, heads_q, seqlen_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_bwd: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  // no gradient may overlap an input, another gradient, or the workspace
+  const int64_t gb = grad_dtype == FA_DTYPE_BF16 ? 2 : 4;
+  uintptr_t lo[10], hi[10];
+  span(q, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[0], &hi[0]);
+  span(o, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[1], &hi[1]);
+  span(dout, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[2], &hi[2]);
+  span(k, kv_stride, batch, heads_kv, seqlen_k, head_dim, 2, &lo[3], &hi[3]);
+  span(v, kv_stride, batch, heads_kv, seqlen_k, head_dim, 2, &lo[4], &hi[4]);
+  lo[5] = reinterpret_cast<uintptr_t>(lse);
+  hi[5] = lo[5] + (uintptr_t)batch * heads_q * seqlen_q * sizeof(float);
+  lo[6] = reinterpret_cast<uintptr_t>(workspace);
+  hi[6] = lo[6] + need;
+  span(dq, dq_stride, batch, heads_q, seqlen_q, head_dim, gb, &lo[7], &hi[7]);
+  span(dk, dkv_stride, batch, heads_kv, seqlen_k, head_dim, gb, &lo[8], &hi[8]);
+  span(dv, dkv_stride, batch, heads_kv, seqlen_k, head_dim, gb, &lo[9], &hi[9]);
+  for (int gi = 7; gi < 10; ++gi)
+    for (int j = 0; j < 10; ++j)
+      if (j != gi && overlap(lo[gi], hi[gi], lo[j], hi[j]))
+        return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: gradient buffers must not overlap inputs, each other or the workspace");
+  if ((int64_t)batch * heads_q * ((seqlen_q + 127) / 128) > 0x7fffffffLL ||
+      (int64_t)batch * heads_q * seqlen_q * (head_dim / 8) > 0x7fffffffLL * 256LL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: problem too large for one launch");
+
+  fa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dsum = static_cast<float*>(workspace);
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  for (int i = 0; i < 3; ++i) {
+    p.q_stride[i] = q_stride[i]; p.kv_stride[i] = kv_stride[i];
+    p.dq_stride[i] = dq_stride[i]; p.dkv_stride[i] = dkv_stride[i];
+  }
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+  p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = mask == FA_MASK_CAUSAL;
+  p.grad_fp32 = grad_dtype == FA_DTYPE_FP32;
+  hipError_t e = fa::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fa_status_string(fa_status_t s) {
   switch (s) {
     case FA_OK: return "FA_OK";

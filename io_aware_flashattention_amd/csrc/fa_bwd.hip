@@ -1,0 +1,320 @@
+// Attention backward for bf16 inputs on gfx950, by recomputation: the
+// probabilities are rebuilt tile by tile from Q, K and the forward pass's
+// per-row log-sum-exp, never stored ("FlashAttention Explained: IO-Aware
+// Attention, Tiling, Online Softmax and FP8 on Hopper", section "Backward
+// Pass: Recomputation Beats Storage"; "How FlashAttention Reduces HBM Traffic
+// Exactly", section "Training: recomputation replaces saved attention
+// probabilities"). With P = exp(scale Q K^T - LSE) and the incoming dO:
+//   D  = rowsum(dO * O)                       (pre-pass, one value per row)
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D)
+//   dK = scale dS^T Q,          dQ = scale dS K
+// Two kernels share the work without atomics, so results are deterministic:
+//   dkdv: a workgroup owns 128 keys of one kv head (32 per wave) and walks the
+//         query rows of every query head of its group, accumulating dK and dV
+//         in registers (the GQA sum happens in place);
+//   dq:   a workgroup owns 128 query rows of one head (32 per wave) and walks
+//         the key tiles, accumulating dQ in registers.
+// Each of the five products runs on v_mfma_f32_32x32x16_bf16. Operand tiles
+// are staged in LDS and read two ways: 16-byte row fragments in sigma order
+// (so the score accumulator comes out in the B-operand layout of the next
+// product, as in the forward kernel) and transposing ds_read_b64_tr_b16
+// reads (the transposed operand of the accumulation products).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int BB = 32;       // rows (or keys) per matrix-core block and per wave
+constexpr int NWB = 4;       // waves per workgroup
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16-byte chunk swizzle of a tile row (any XOR pattern is correct as long as
+// every access of row r uses this row's value)
+template <int D> __device__ __forceinline__ int bswz(int r) {
+  return D == 128 ? (sigma32(r & 31) & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int tile_off(int r, int c) {   // element offset of (row, column)
+  return r * D + 8 * ((c >> 3) ^ bswz<D>(r)) + (c & 7);
+}
+
+// Copy rows [r0, r0+32) of a row-major global matrix (row stride rs elements)
+// into a 32 x D LDS tile; rows at or past `rows` are zero.
+template <int D>
+__device__ __forceinline__ void stage(__bf16* t, const __bf16* g, int64_t rs, int r0, int rows, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = tid; i < BB * CPR; i += NWB * 64) {
+    const int r = i / CPR, c = i % CPR;
+    const u32x4 v = r0 + r < rows ? load16(g + (int64_t)(r0 + r) * rs + 8 * c) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(t + tile_off<D>(r, 8 * c)) = v;
+  }
+}
+
+// A operand of X Y^T with X a 32-row LDS tile read in sigma order: lane l
+// gets row sigma(l % 32), elements 16 kc + 8 (l / 32) .. +7.
+template <int D> __device__ __forceinline__ bf16x8 frag_sigma(const __bf16* t, int lane, int kc) {
+  const int r = sigma32(lane & 31);
+  return *reinterpret_cast<const bf16x8*>(t + tile_off<D>(r, 16 * kc + 8 * (lane >> 5)));
+}
+
+// A operand of X^T Z for a 32-row LDS tile X: rows 16 c .. 16 c + 15 of X as
+// the K dimension, columns 32 db .. 32 db + 31 as M (two transposing reads).
+template <int D> __device__ __forceinline__ bf16x8 frag_trans(const __bf16* t, int lane, int db, int c) {
+  const int gg = lane >> 4, i = lane & 15;
+  const int r = 16 * c + 8 * (gg >> 1) + (i >> 2);
+  const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + tile_off<D>(r, col)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + tile_off<D>(r + 4, col)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One row of a global row-major matrix as B operands: lane l holds row
+// `row` (its own), elements 16 kc + 8 (l / 32) .. +7; zero past `rows`.
+template <int D>
+__device__ __forceinline__ void load_rowfrags(bf16x8 (&f)[D / 16], const __bf16* g, int64_t rs, int row, int rows,
+                                              int lane) {
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc)
+    f[kc] = as_bf16x8(row < rows ? load16(g + (int64_t)row * rs + 16 * kc + 8 * (lane >> 5)) : u32x4{0, 0, 0, 0});
+}
+
+// Transposed accumulator (32 x 32 block of [d, row]) to a row: lane l owns
+// row l % 32 and writes d = 32 db + 8 gq + 4 (l / 32) .. +3.
+template <int D, typename TOut>
+__device__ __forceinline__ void store_rows(TOut* dst, const f32x16 (&acc)[D / 32], float mul, int lane) {
+  const int half = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * db + 8 * gq + 4 * half;
+      const float v0 = acc[db][4 * gq] * mul, v1 = acc[db][4 * gq + 1] * mul;
+      const float v2 = acc[db][4 * gq + 2] * mul, v3 = acc[db][4 * gq + 3] * mul;
+      if constexpr (sizeof(TOut) == 4) {
+        *reinterpret_cast<f32x4*>(dst + d) = f32x4{v0, v1, v2, v3};
+      } else {
+        bf16x4 h;
+        h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
+        *reinterpret_cast<bf16x4*>(dst + d) = h;
+      }
+    }
+}
+
+}  // namespace
+
+namespace detail {
+
+// D[b, h, i] = sum_d dO[i, d] * O[i, d]: 16 lanes per row, 16 bytes each
+// (head_dim 128; 8 lanes for 64).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;                 // lanes per row
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int c = (int)(gid % LPR);
+  float s = 0.f;
+  if (row < rows) {
+    const int i = (int)(row % p.seqlen_q);
+    const int64_t bh = row / p.seqlen_q;
+    const int h = (int)(bh % p.heads_q), b = (int)(bh / p.heads_q);
+    const int64_t off = (int64_t)b * p.q_stride[0] + (int64_t)h * p.q_stride[1] + (int64_t)i * p.q_stride[2] + 8 * c;
+    const bf16x8 o = as_bf16x8(load16(reinterpret_cast<const __bf16*>(p.o) + off));
+    const bf16x8 g = as_bf16x8(load16(reinterpret_cast<const __bf16*>(p.dout) + off));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf((float)o[e], (float)g[e], s);
+  }
+#pragma unroll
+  for (int w = 1; w < LPR; w <<= 1) s += __shfl_xor(s, w, LPR);
+  if (row < rows && c == 0) p.dsum[row] = s;
+}
+
+// dK and dV for 128 keys of one (batch, kv head).
+template <int D, bool CAUSAL, typename TOut>
+__global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int KS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 qs[BB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 gs[BB * D];      // dO
+  __shared__ __attribute__((aligned(16))) float ls[BB];           // LSE * log2(e) (+inf past the end)
+  __shared__ __attribute__((aligned(16))) float ds[BB];           // D
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int ktiles = (p.seqlen_k + NWB * BB - 1) / (NWB * BB);
+  const int kt = blockIdx.x % ktiles;
+  const int bk = blockIdx.x / ktiles;
+  const int kvh = bk % p.heads_kv, b = bk / p.heads_kv;
+  const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int k0 = kt * NWB * BB;
+  const int kw0 = k0 + wave * BB;            // this wave's keys kw0 .. kw0 + 31
+  const int key = kw0 + (lane & 31);
+
+  const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
+  const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
+  bf16x8 kf[KS], vf[KS];
+  load_rowfrags<D>(kf, kp, p.kv_stride[2], key, nk, lane);
+  load_rowfrags<D>(vf, vp, p.kv_stride[2], key, nk, lane);
+
+  f32x16 dv[DB], dk[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dv[i] = dk[i] = f32x16{};
+
+  const float c2 = p.scale_log2;
+  const int r_begin = CAUSAL ? k0 : 0;       // earlier rows see none of these keys
+  for (int g = 0; g < p.group; ++g) {
+    const int hq = kvh * p.group + g;
+    const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + qo;
+    const __bf16* gp = reinterpret_cast<const __bf16*>(p.dout) + qo;
+    const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
+    for (int r0 = r_begin; r0 < nq; r0 += BB) {
+      __syncthreads();                       // previous block's readers are done
+      stage<D>(qs, qp, p.q_stride[2], r0, nq, tid);
+      stage<D>(gs, gp, p.q_stride[2], r0, nq, tid);
+      if (tid < BB) {
+        const int r = r0 + tid;
+        ls[tid] = r < nq ? p.lse[so + r] * kLog2e : __builtin_huge_valf();
+        ds[tid] = r < nq ? p.dsum[so + r] : 0.f;
+      }
+      __syncthreads();
+      if (CAUSAL && kw0 > r0 + BB - 1) continue;   // every key of this wave is in these rows' future
+
+      // S and dP for (rows, keys): accumulator register j holds row acc_key(j, half), key = lane % 32
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KS; ++kc) {
+        s = mfma32(frag_sigma<D>(qs, lane, kc), kf[kc], s);
+        dp = mfma32(frag_sigma<D>(gs, lane, kc), vf[kc], dp);
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rr = acc_key(j, half);
+        const int row = r0 + rr;
+        const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
+        const float pr = vis ? fast_exp2(fmaf(s[j], c2, -ls[rr])) : 0.f;
+        const float dsv = pr * (dp[j] - ds[rr]);
+        pb[j >> 3][j & 7] = (__bf16)pr;
+        sb[j >> 3][j & 7] = (__bf16)dsv;
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (rows are the contraction)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(frag_trans<D>(gs, lane, db, c), pb[c], dv[db]);
+          dk[db] = mfma32(frag_trans<D>(qs, lane, db, c), sb[c], dk[db]);
+        }
+    }
+  }
+  if (key < nk) {
+    const int64_t o = (int64_t)b * p.dkv_stride[0] + (int64_t)kvh * p.dkv_stride[1] + (int64_t)key * p.dkv_stride[2];
+    store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dk) + o, dk, p.scale, lane);
+    store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dv) + o, dv, 1.f, lane);
+  }
+}
+
+// dQ for 128 query rows of one (batch, query head).
+template <int D, bool CAUSAL, typename TOut>
+__global__ __launch_bounds__(NWB * 64) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int KS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[BB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[BB * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int qtiles = (p.seqlen_q + NWB * BB - 1) / (NWB * BB);
+  const int qt = blockIdx.x % qtiles;
+  const int bh = blockIdx.x / qtiles;
+  const int hq = bh % p.heads_q, b = bh / p.heads_q;
+  const int kvh = hq / p.group;
+  const int nq = p.seqlen_q, nk = p.seqlen_k;
+  const int q0 = qt * NWB * BB;
+  const int rw0 = q0 + wave * BB;
+  const int row = rw0 + (lane & 31);
+
+  const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
+  bf16x8 qf[KS], gf[KS];
+  load_rowfrags<D>(qf, reinterpret_cast<const __bf16*>(p.q) + qo, p.q_stride[2], row, nq, lane);
+  load_rowfrags<D>(gf, reinterpret_cast<const __bf16*>(p.dout) + qo, p.q_stride[2], row, nq, lane);
+  const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
+  const float lse2 = row < nq ? p.lse[so + row] * kLog2e : __builtin_huge_valf();
+  const float dsum = row < nq ? p.dsum[so + row] : 0.f;
+
+  const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
+  const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  const float c2 = p.scale_log2;
+  const int k_end = CAUSAL ? min(nk, q0 + NWB * BB) : nk;
+  for (int kv0 = 0; kv0 < k_end; kv0 += BB) {
+    __syncthreads();
+    stage<D>(ks, kp, p.kv_stride[2], kv0, nk, tid);
+    stage<D>(vs, vp, p.kv_stride[2], kv0, nk, tid);
+    __syncthreads();
+    if (CAUSAL && kv0 > rw0 + BB - 1) continue;    // these keys are in the future of every row of the wave
+
+    // S^T and dP^T for (keys, rows): register j holds key acc_key(j, half), row = lane % 32
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KS; ++kc) {
+      s = mfma32(frag_sigma<D>(ks, lane, kc), qf[kc], s);
+      dp = mfma32(frag_sigma<D>(vs, lane, kc), gf[kc], dp);
+    }
+    bf16x8 sb[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = kv0 + acc_key(j, half);
+      const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
+      const float pr = vis ? fast_exp2(fmaf(s[j], c2, -lse2)) : 0.f;
+      sb[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dsum));
+    }
+    // dQ^T += K^T dS^T (keys are the contraction)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq[db] = mfma32(frag_trans<D>(ks, lane, db, c), sb[c], dq[db]);
+  }
+  if (row < nq) {
+    const int64_t o = (int64_t)b * p.dq_stride[0] + (int64_t)hq * p.dq_stride[1] + (int64_t)row * p.dq_stride[2];
+    store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dq) + o, dq, p.scale, lane);
+  }
+}
+
+}  // namespace detail
+
+namespace {
+
+template <int D, bool CAUSAL, typename TOut>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
+  const int64_t pre_threads = rows * (D / 8);
+  hipLaunchKernelGGL((detail::bwd_pre_kernel<D>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t kwg = (int64_t)p.batch * p.heads_kv * ((p.seqlen_k + NWB * BB - 1) / (NWB * BB));
+  hipLaunchKernelGGL((detail::bwd_dkdv_kernel<D, CAUSAL, TOut>), dim3((unsigned)kwg), dim3(NWB * 64), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t qwg = (int64_t)p.batch * p.heads_q * ((p.seqlen_q + NWB * BB - 1) / (NWB * BB));
+  hipLaunchKernelGGL((detail::bwd_dq_kernel<D, CAUSAL, TOut>), dim3((unsigned)qwg), dim3(NWB * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  return p.grad_fp32 ? launch_bwd_t<D, CAUSAL, float>(p, stream) : launch_bwd_t<D, CAUSAL, __bf16>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.head_dim == 64) return p.causal ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
+  return p.causal ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
+}
+
+}  // namespace fa

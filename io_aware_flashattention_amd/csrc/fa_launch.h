@@ -47,9 +47,28 @@ struct DecodeParams {
   bool out_fp32;
 };
 
+struct BwdParams {
+  const void* q;       // [B, Hq, Nq, d] bf16, strides q_stride (shared by o, dout)
+  const void* k;       // [B, Hkv, Nk, d] bf16, strides kv_stride (shared by v)
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // [B, Hq, Nq] natural log, from the forward pass
+  float* dsum;         // workspace [B, Hq, Nq]: rowsum(dO * O)
+  void* dq;            // strides dq_stride
+  void* dk;            // strides dkv_stride (shared by dv)
+  void* dv;
+  int64_t q_stride[3], kv_stride[3], dq_stride[3], dkv_stride[3];
+  int batch, heads_q, heads_kv, group, seqlen_q, seqlen_k, head_dim;
+  float scale, scale_log2;
+  bool causal, grad_fp32;
+};
+
 // n_qtiles is filled in by the launchers (it depends on the kernel's row tile).
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);       // dispatches on in_fp32
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 int decode_waves();
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

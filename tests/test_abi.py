@@ -114,6 +114,50 @@ def test_fwd_varlen_rejects_before_launch(kw, status, needle):
     assert needle in msg
 
 
+def _bwd(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, do=FAKE + 0x400000,
+             lse=FAKE + 0x500000, dq=FAKE + 0x600000, dk=FAKE + 0x700000, dv=FAKE + 0x800000, B=1, Hq=4, Hkv=2,
+             Nq=64, Nk=64, d=128, qs=(4 * 64 * 128, 64 * 128, 128), ks=(2 * 64 * 128, 64 * 128, 128),
+             dqs=(4 * 64 * 128, 64 * 128, 128), dks=(2 * 64 * 128, 64 * 128, 128), gd=1, mask=1, scale=0.125,
+             ws=FAKE + 0x900000, wsb=1 << 20)
+    a.update(kw)
+    arr = lambda t: (ctypes.c_int64 * 3)(*t) if t is not None else None
+    st = lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                    a["Hkv"], a["Nq"], a["Nk"], a["d"], arr(a["qs"]), arr(a["ks"]), arr(a["dqs"]), arr(a["dks"]),
+                    a["gd"], a["mask"], a["scale"], a["ws"], a["wsb"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(do=None), 1, "non-null"),
+    (dict(dks=None), 1, "stride"),
+    (dict(Nk=0), 1, "positive"),
+    (dict(gd=5), 1, "grad_dtype"),
+    (dict(mask=2), 1, "mask"),
+    (dict(scale=float("nan")), 1, "softmax_scale"),
+    (dict(d=32), 2, "head_dim"),
+    (dict(Hq=6, Hkv=4), 2, "multiple"),
+    (dict(Nq=64, Nk=96), 2, "causal"),
+    (dict(lse=FAKE + 0x500004), 2, "aligned"),
+    (dict(qs=(4 * 64 * 128, 64 * 128, 132)), 2, "input strides"),
+    (dict(dqs=(4 * 64 * 128, 64 * 128, 130)), 2, "gradient strides"),
+    (dict(wsb=100), 3, "workspace"),
+    (dict(dk=FAKE + 0x100000), 1, "overlap"),
+    (dict(dv=FAKE + 0x700100), 1, "overlap"),
+])
+def test_bwd_rejects_before_launch(kw, status, needle):
+    st, msg = _bwd(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_bwd_workspace_size():
+    lib = _lib.load()
+    assert lib.fa_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert lib.fa_bwd_workspace_bytes(0, 8, 100) == 0
+
+
 def _dec(**kw):
     lib = _lib.load()
     a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lens=FAKE + 0x300000, o=FAKE + 0x400000, lse=None,

@@ -1,0 +1,103 @@
+"""GPU parity of fa_bwd (through the C ABI) against the fp64 oracle's backward.
+
+The forward pass runs on the GPU first (its bf16 O and float32 LSE are what a
+training step would hand to the backward), then dQ, dK and dV are compared
+with attention_bwd_ref on the same bf16 inputs and dO.
+
+Bar (derived from the arithmetic, see the design notes): the kernels feed
+bf16-rounded P and dS (relative error <= 2^-9 each) to float32-accumulating
+matrix cores, and D = rowsum(dO * O) uses the bf16-rounded O. Each gradient
+element is a sum of such terms, so its error is bounded by about 2^-8 times
+the sum of the magnitudes of its terms; over whole tensors this stays below
+1% of the largest gradient element and 0.4% of the mean magnitude. The gate
+is max|err| <= 1e-2 * max|ref| and mean|err| <= 4e-3 * mean|ref| per tensor
+(normalisers floored at 1e-2 and 1e-3: a row with one visible key has dS = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_flashattention_amd import workloads as W
+from oracle import attention_bwd_ref
+from tests.parity import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL = 1e-2, 4e-3
+
+
+def fa():
+    import io_aware_flashattention_amd as m
+    return m
+
+
+def check_grad(got, ref, what):
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    err = np.abs(g - ref)
+    # normalisers floored: with one visible key dS is exactly 0 and so are dQ and dK
+    mx = err.max() / max(np.abs(ref).max(), 1e-2)
+    mn = err.mean() / max(np.abs(ref).mean(), 1e-3)
+    say(f"  {what}: max|err|/max|ref| {mx:.2e}  mean|err|/mean|ref| {mn:.2e}")
+    assert mx <= MAX_REL and mn <= MEAN_REL, f"{what}: {mx:.3e} {mn:.3e}"
+
+
+def run_case(B, Hq, Hkv, N, d, causal, seed, grad_dtype=torch.float32):
+    q, k, v = W.make_random_prefill(B, Hq, Hkv, N, N, d, seed=seed)
+    g, _, _ = W.make_random_prefill(B, Hq, Hkv, N, N, d, seed=seed + 1)      # dO
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa().fwd(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa().bwd(qd, kd, vd, o, gd, lse, causal=causal, scale=scale, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = attention_bwd_ref(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(g), scale, causal=causal)
+    return (dq, dk, dv), (rq, rk, rv), (qd, kd, vd, o, gd, lse, scale)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 31, 33, 100, 129, 300])
+def test_bwd_small(d, causal, N):
+    say(f"case bwd B=2 Hq=4 Hkv=2 N={N} d={d} causal={causal}")
+    got, ref, _ = run_case(2, 4, 2, N, d, causal, seed=900 + N + d)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(a, b, f"{name} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_gqa_2k(causal):
+    """Eight query heads over two kv heads at 2048 tokens: dK and dV sum four
+    query heads each, over 64 key tiles and query tiles."""
+    say(f"case bwd B=1 Hq=8 Hkv=2 N=2048 d=128 causal={causal}")
+    got, ref, _ = run_case(1, 8, 2, 2048, 128, causal, seed=950)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(a, b, f"{name} 2k causal={causal}")
+
+
+def test_bwd_bf16_grads_are_rounded_fp32_grads():
+    say("case bwd bf16 gradients == RNE(fp32 gradients)")
+    got32, _, (qd, kd, vd, o, gd, lse, scale) = run_case(1, 4, 4, 200, 128, True, seed=960)
+    dq16, dk16, dv16 = fa().bwd(qd, kd, vd, o, gd, lse, causal=True, scale=scale, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for a, b in zip((dq16, dk16, dv16), got32):
+        assert torch.equal(a, b.to(torch.bfloat16))
+
+
+def test_bwd_deterministic_and_gqa_matches_replicated_heads():
+    """Two runs give identical bits; dK and dV of a shared kv head equal the sums
+    over explicitly replicated kv heads."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 160, 64
+    say("case bwd determinism and GQA vs replicated heads")
+    got, _, (qd, kd, vd, o, gd, lse, scale) = run_case(B, Hq, Hkv, N, d, True, seed=970)
+    again = fa().bwd(qd, kd, vd, o, gd, lse, causal=True, scale=scale, grad_dtype=torch.float32)
+    kr = kd.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    vr = vd.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    rq, rk, rv = fa().bwd(qd, kr, vr, o, gd, lse, causal=True, scale=scale, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(got, again):
+        assert torch.equal(a, b)
+    assert torch.equal(rq, got[0])
+    rk_sum = rk.view(B, Hkv, Hq // Hkv, N, d).sum(dim=2)
+    rv_sum = rv.view(B, Hkv, Hq // Hkv, N, d).sum(dim=2)
+    assert (rk_sum - got[1]).abs().max().item() <= 1e-5 * max(1.0, got[1].abs().max().item())
+    assert (rv_sum - got[2]).abs().max().item() <= 1e-5 * max(1.0, got[2].abs().max().item())
