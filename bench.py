@@ -7,12 +7,13 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
      kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
      and merge kernel).
-After the timed steps, three more paths are timed on their own (not part of
+After the timed steps, four more paths are timed on their own (not part of
 the step): the same decode against a paged cache (fa_decode_paged: 16-token
 pages in a token-major pool, shuffled block table) as ``decode_paged``, and
 through fa_fwd_varlen the 8192-token sliding-window-1024 prefill
 (``prefill_window``) and a packed batch of 16 causal sequences of 1..8192
-tokens (``prefill_varlen``).
+tokens (``prefill_varlen``), and the backward of the step's prefill through
+fa_bwd (``backward``, 2.5x the forward FLOPs).
 Inputs are generated and uploaded before the timed region. W untimed warmup
 steps, then exactly K timed steps between two device synchronisations. Kernel
 durations come from HIP events recorded on the stream the kernels run on.
@@ -193,6 +194,22 @@ def run(args):
                                   + (f"causal window {win}" if win is not None else "causal"),
                       "kernel": "fa_fwd_varlen"}
         del vq, vk, vv, vo
+    # backward of the step's prefill (same inputs, its O and LSE, a seeded dO)
+    gh, _, _ = W.make_random_prefill(pc.batch, pc.heads_q, pc.heads_kv, pc.seqlen, pc.seqlen, pc.head_dim,
+                                     seed=pc.seed + 100)
+    dout = to_dev(gh)
+    fa.fwd(q, k, v, causal=True, scale=pc.scale, out=o, lse=lse)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(fa.load().fa_bwd_workspace_bytes(pc.batch, pc.heads_q, pc.seqlen), dtype=torch.uint8,
+                      device=dev)
+    ms = time_launches(lambda: fa.bwd(q, k, v, o, dout, lse, causal=True, scale=pc.scale, dq=gq, dk=gk, dv=gv,
+                                      workspace=bws))
+    fl = cm.backward_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)
+    extra["backward"] = {"ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                         "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "flops_per_launch": fl, "workload": "causal GQA B1 Hq64 Hkv8 N8192 d128, bf16 gradients",
+                         "kernel": "fa_bwd (pre-pass + dK/dV + dQ)"}
+    del dout, gq, gk, gv, bws
 
     pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
     kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
@@ -305,9 +322,10 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
     """Label per-dispatch rows (sorted by Dispatch_Id) with the bench phase
     they belong to. The bench launches, in this order: n_launch steps of
     (prefill, decode split, decode merge); n_launch paged decodes (paged split,
-    merge); n_launch window prefills; n_launch packed prefills. The prefill
-    kernel is the same instantiation for the last three, so the phase comes
-    from the dispatch order."""
+    merge); n_launch window prefills; n_launch packed prefills; one prefill
+    for the backward's inputs, then n_launch backward passes. The prefill
+    kernel is the same instantiation in every prefill phase, so the phase
+    comes from the dispatch order."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     seen = {"fwd": 0, "merge": 0}
     out = []
@@ -316,7 +334,10 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
         if re.search(r"fwd_\w*kernel", name):
             i = seen["fwd"]
             seen["fwd"] += 1
-            label = ("prefill c4a (step)", "prefill window c7", "prefill varlen c6")[min(2, i // n_launch)]
+            label = ("prefill c4a (step)", "prefill window c7", "prefill varlen c6",
+                     "prefill c4a (backward inputs)")[min(3, i // n_launch)]
+        elif "bwd_" in name:
+            label = "backward " + re.sub(r".*(bwd_\w+?_kernel).*", r"\1", name)
         elif "decode_split" in name:            # contiguous: template flag false (mangled "Lb0E")
             label = "decode split (step)" if ("Lb0E" in name or "false" in name) else "paged decode split"
         elif "decode_merge" in name:

@@ -30,6 +30,13 @@ def attention_flops(batch: int, heads_q: int, seqlen_q: int, seqlen_k: int, head
     return f / 2.0 if causal else f
 
 
+def backward_flops(batch: int, heads_q: int, seqlen_q: int, seqlen_k: int, head_dim: int, causal: bool) -> float:
+    """Algorithmic FLOPs of the backward pass: five matmuls (QK^T recomputed, dV,
+    dP, dQ, dK) against the forward's two, so 2.5x attention_flops ("FlashAttention
+    Explained", section "Backward Pass: Recomputation Beats Storage")."""
+    return 2.5 * attention_flops(batch, heads_q, seqlen_q, seqlen_k, head_dim, causal)
+
+
 def window_flops(heads_q: int, seqlen: int, head_dim: int, window: int) -> float:
     """Algorithmic FLOPs of one sequence under a sliding window W on top of the
     causal mask: 4 * d per visible (row, key) pair, counted exactly (row r sees

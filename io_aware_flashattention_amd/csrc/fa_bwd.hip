@@ -11,9 +11,12 @@
 // Two kernels share the work without atomics, so results are deterministic:
 //   dkdv: a workgroup owns 128 keys of one kv head (32 per wave) and walks the
 //         query rows of every query head of its group, accumulating dK and dV
-//         in registers (the GQA sum happens in place);
+//         in registers (the GQA sum happens in place); under the causal mask
+//         it takes key tiles t and T-1-t so every workgroup has equal work;
 //   dq:   a workgroup owns 128 query rows of one head (32 per wave) and walks
 //         the key tiles, accumulating dQ in registers.
+// Both stream their operand tiles 64 rows at a time through LDS, the next 64
+// rows held in registers while the current ones feed the matrix cores.
 // Each of the five products runs on v_mfma_f32_32x32x16_bf16. Operand tiles
 // are staged in LDS and read two ways: 16-byte row fragments in sigma order
 // (so the score accumulator comes out in the B-operand layout of the next
@@ -32,7 +35,9 @@ constexpr int NWB = 4;       // waves per workgroup
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // 16-byte chunk swizzle of a tile row (any XOR pattern is correct as long as
-// every access of row r uses this row's value)
+// every access of row r uses this row's value). It depends on r % 32 only,
+// so a 32-row block at row offset 32 b of a taller tile is addressed as a
+// 32-row tile at t + 32 b D.
 template <int D> __device__ __forceinline__ int bswz(int r) {
   return D == 128 ? (sigma32(r & 31) & 15) : ((r >> 1) & 7);
 }
@@ -40,18 +45,32 @@ template <int D> __device__ __forceinline__ int tile_off(int r, int c) {   // el
   return r * D + 8 * ((c >> 3) ^ bswz<D>(r)) + (c & 7);
 }
 
-// Copy rows [r0, r0+32) of a row-major global matrix (row stride rs elements)
-// into a 32 x D LDS tile; rows at or past `rows` are zero.
-template <int D>
-__device__ __forceinline__ void stage(__bf16* t, const __bf16* g, int64_t rs, int r0, int rows, int tid) {
-  constexpr int CPR = D / 8;
+// Rows [r0, r0 + ROWS) of a row-major global matrix (row stride rs
+// elements) held in registers on their way to a ROWS x D LDS tile: load()
+// issues the global reads (rows at or past `rows` are zero) early, store()
+// writes them to LDS once the tile's previous readers are done, so the
+// global latency hides behind a block of matrix work.
+template <int D, int ROWS>
+struct Prefetch {
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int N = ROWS * CPR / (NWB * 64);       // per thread
+  static_assert(ROWS * CPR % (NWB * 64) == 0, "");
+  u32x4 v[N];
+  __device__ __forceinline__ void load(const __bf16* g, int64_t rs, int r0, int rows, int tid) {
 #pragma unroll
-  for (int i = tid; i < BB * CPR; i += NWB * 64) {
-    const int r = i / CPR, c = i % CPR;
-    const u32x4 v = r0 + r < rows ? load16(g + (int64_t)(r0 + r) * rs + 8 * c) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(t + tile_off<D>(r, 8 * c)) = v;
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + NWB * 64 * i, r = idx / CPR, c = idx % CPR;
+      v[i] = r0 + r < rows ? load16(g + (int64_t)(r0 + r) * rs + 8 * c) : u32x4{0, 0, 0, 0};
+    }
   }
-}
+  __device__ __forceinline__ void store(__bf16* t, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + NWB * 64 * i, r = idx / CPR, c = idx % CPR;
+      *reinterpret_cast<u32x4*>(t + tile_off<D>(r, 8 * c)) = v[i];
+    }
+  }
+};
 
 // A operand of X Y^T with X a 32-row LDS tile read in sigma order: lane l
 // gets row sigma(l % 32), elements 16 kc + 8 (l / 32) .. +7.
@@ -69,16 +88,6 @@ template <int D> __device__ __forceinline__ bf16x8 frag_trans(const __bf16* t, i
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + tile_off<D>(r, col)));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + tile_off<D>(r + 4, col)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// One row of a global row-major matrix as B operands: lane l holds row
-// `row` (its own), elements 16 kc + 8 (l / 32) .. +7; zero past `rows`.
-template <int D>
-__device__ __forceinline__ void load_rowfrags(bf16x8 (&f)[D / 16], const __bf16* g, int64_t rs, int row, int rows,
-                                              int lane) {
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc)
-    f[kc] = as_bf16x8(row < rows ? load16(g + (int64_t)row * rs + 16 * kc + 8 * (lane >> 5)) : u32x4{0, 0, 0, 0});
 }
 
 // Transposed accumulator (32 x 32 block of [d, row]) to a row: lane l owns
@@ -132,101 +141,130 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   if (row < rows && c == 0) p.dsum[row] = s;
 }
 
-// dK and dV for 128 keys of one (batch, kv head).
+// dK and dV for 128 keys of one (batch, kv head), walking the query rows 64
+// at a time (two 32-row blocks) with the next 64 rows prefetched. Under the
+// causal mask key tile t sees the rows from 128 t on, so a workgroup takes
+// tiles t and T-1-t in turn and every workgroup does the same amount of work.
 template <int D, bool CAUSAL, typename TOut>
 __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[BB * D];
-  __shared__ __attribute__((aligned(16))) __bf16 gs[BB * D];      // dO
-  __shared__ __attribute__((aligned(16))) float ls[BB];           // LSE * log2(e) (+inf past the end)
-  __shared__ __attribute__((aligned(16))) float ds[BB];           // D
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * BB;
+  __shared__ __attribute__((aligned(16))) __bf16 qs[RB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 gs[RB * D];      // dO
+  __shared__ __attribute__((aligned(16))) float ls[RB];           // LSE * log2(e) (+inf past the end)
+  __shared__ __attribute__((aligned(16))) float ds[RB];           // D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int ktiles = (p.seqlen_k + NWB * BB - 1) / (NWB * BB);
-  const int kt = blockIdx.x % ktiles;
-  const int bk = blockIdx.x / ktiles;
+  const int units = CAUSAL ? (ktiles + 1) / 2 : ktiles;
+  const int u = blockIdx.x % units;
+  const int bk = blockIdx.x / units;
   const int kvh = bk % p.heads_kv, b = bk / p.heads_kv;
   const int nq = p.seqlen_q, nk = p.seqlen_k;
-  const int k0 = kt * NWB * BB;
-  const int kw0 = k0 + wave * BB;            // this wave's keys kw0 .. kw0 + 31
-  const int key = kw0 + (lane & 31);
-
+  const float c2 = p.scale_log2;
   const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
   const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
-  bf16x8 kf[KS], vf[KS];
-  load_rowfrags<D>(kf, kp, p.kv_stride[2], key, nk, lane);
-  load_rowfrags<D>(vf, vp, p.kv_stride[2], key, nk, lane);
+  Prefetch<D, RB> pq, pg;
+  float pl = 0.f, pd = 0.f;
 
-  f32x16 dv[DB], dk[DB];
+  for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+    const int kt = pass == 0 ? u : ktiles - 1 - u;
+    if (pass == 1 && kt == u) break;         // odd tile count: the middle tile has no partner
+    const int k0 = kt * NWB * BB;
+    const int kw0 = k0 + wave * BB;          // this wave's keys kw0 .. kw0 + 31
+    const int key = kw0 + (lane & 31);
+    bf16x8 kf[KS], vf[KS];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) dv[i] = dk[i] = f32x16{};
+    for (int kc = 0; kc < KS; ++kc) {
+      kf[kc] = as_bf16x8(key < nk ? load16(kp + (int64_t)key * p.kv_stride[2] + 16 * kc + 8 * half) : u32x4{0, 0, 0, 0});
+      vf[kc] = as_bf16x8(key < nk ? load16(vp + (int64_t)key * p.kv_stride[2] + 16 * kc + 8 * half) : u32x4{0, 0, 0, 0});
+    }
+    f32x16 dv[DB], dk[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) dv[i] = dk[i] = f32x16{};
 
-  const float c2 = p.scale_log2;
-  const int r_begin = CAUSAL ? k0 : 0;       // earlier rows see none of these keys
-  for (int g = 0; g < p.group; ++g) {
-    const int hq = kvh * p.group + g;
-    const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + qo;
-    const __bf16* gp = reinterpret_cast<const __bf16*>(p.dout) + qo;
-    const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
-    for (int r0 = r_begin; r0 < nq; r0 += BB) {
-      __syncthreads();                       // previous block's readers are done
-      stage<D>(qs, qp, p.q_stride[2], r0, nq, tid);
-      stage<D>(gs, gp, p.q_stride[2], r0, nq, tid);
-      if (tid < BB) {
+    const int r_begin = CAUSAL ? k0 : 0;     // earlier rows see none of these keys
+    const int nblk = (nq - r_begin + RB - 1) / RB;
+    const int total = p.group * nblk;        // (query head, row block) steps
+    auto fetch = [&](int step) {
+      const int g = step / nblk, r0 = r_begin + (step % nblk) * RB;
+      const int hq = kvh * p.group + g;
+      const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
+      pq.load(reinterpret_cast<const __bf16*>(p.q) + qo, p.q_stride[2], r0, nq, tid);
+      pg.load(reinterpret_cast<const __bf16*>(p.dout) + qo, p.q_stride[2], r0, nq, tid);
+      if (tid < RB) {
+        const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
         const int r = r0 + tid;
-        ls[tid] = r < nq ? p.lse[so + r] * kLog2e : __builtin_huge_valf();
-        ds[tid] = r < nq ? p.dsum[so + r] : 0.f;
+        pl = r < nq ? p.lse[so + r] * kLog2e : __builtin_huge_valf();
+        pd = r < nq ? p.dsum[so + r] : 0.f;
+      }
+    };
+    if (total > 0) fetch(0);
+    for (int step = 0; step < total; ++step) {
+      const int r0 = r_begin + (step % nblk) * RB;
+      __syncthreads();                       // the previous step's readers are done
+      pq.store(qs, tid);
+      pg.store(gs, tid);
+      if (tid < RB) {
+        ls[tid] = pl;
+        ds[tid] = pd;
       }
       __syncthreads();
-      if (CAUSAL && kw0 > r0 + BB - 1) continue;   // every key of this wave is in these rows' future
-
-      // S and dP for (rows, keys): accumulator register j holds row acc_key(j, half), key = lane % 32
-      f32x16 s = f32x16{}, dp = f32x16{};
+      if (step + 1 < total) fetch(step + 1); // in flight during this step's matrix work
 #pragma unroll
-      for (int kc = 0; kc < KS; ++kc) {
-        s = mfma32(frag_sigma<D>(qs, lane, kc), kf[kc], s);
-        dp = mfma32(frag_sigma<D>(gs, lane, kc), vf[kc], dp);
-      }
-      bf16x8 pb[2], sb[2];
+      for (int sb = 0; sb < 2; ++sb) {
+        const int rs0 = r0 + sb * BB;
+        if (CAUSAL && kw0 > rs0 + BB - 1) continue;   // every key of this wave is in these rows' future
+        const __bf16* qt = qs + sb * BB * D;
+        const __bf16* gt = gs + sb * BB * D;
+        // S and dP for (rows, keys): register j holds row acc_key(j, half), key = lane % 32
+        f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int rr = acc_key(j, half);
-        const int row = r0 + rr;
-        const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
-        const float pr = vis ? fast_exp2(fmaf(s[j], c2, -ls[rr])) : 0.f;
-        const float dsv = pr * (dp[j] - ds[rr]);
-        pb[j >> 3][j & 7] = (__bf16)pr;
-        sb[j >> 3][j & 7] = (__bf16)dsv;
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (rows are the contraction)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(frag_trans<D>(gs, lane, db, c), pb[c], dv[db]);
-          dk[db] = mfma32(frag_trans<D>(qs, lane, db, c), sb[c], dk[db]);
+        for (int kc = 0; kc < KS; ++kc) {
+          sa = mfma32(frag_sigma<D>(qt, lane, kc), kf[kc], sa);
+          dp = mfma32(frag_sigma<D>(gt, lane, kc), vf[kc], dp);
         }
+        bf16x8 pb[2], sbf[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int rr = sb * BB + acc_key(j, half);
+          const int row = r0 + rr;
+          const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
+          const float pr = vis ? fast_exp2(fmaf(sa[j], c2, -ls[rr])) : 0.f;
+          pb[j >> 3][j & 7] = (__bf16)pr;
+          sbf[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - ds[rr]));
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (rows are the contraction)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(frag_trans<D>(gt, lane, db, c), pb[c], dv[db]);
+            dk[db] = mfma32(frag_trans<D>(qt, lane, db, c), sbf[c], dk[db]);
+          }
+      }
     }
-  }
-  if (key < nk) {
-    const int64_t o = (int64_t)b * p.dkv_stride[0] + (int64_t)kvh * p.dkv_stride[1] + (int64_t)key * p.dkv_stride[2];
-    store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dk) + o, dk, p.scale, lane);
-    store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dv) + o, dv, 1.f, lane);
+    if (key < nk) {
+      const int64_t o = (int64_t)b * p.dkv_stride[0] + (int64_t)kvh * p.dkv_stride[1] + (int64_t)key * p.dkv_stride[2];
+      store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dk) + o, dk, p.scale, lane);
+      store_rows<D, TOut>(reinterpret_cast<TOut*>(p.dv) + o, dv, 1.f, lane);
+    }
   }
 }
 
-// dQ for 128 query rows of one (batch, query head).
+// dQ for 128 query rows of one (batch, query head), walking the keys 64 at a
+// time (two 32-key blocks) with the next 64 prefetched. Under the causal
+// mask the heaviest query tiles are dispatched first.
 template <int D, bool CAUSAL, typename TOut>
 __global__ __launch_bounds__(NWB * 64) void bwd_dq_kernel(const BwdParams p) {
-  constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[BB * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[BB * D];
+  constexpr int KS = D / 16, DB = D / 32, KB2 = 2 * BB;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[KB2 * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[KB2 * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int qtiles = (p.seqlen_q + NWB * BB - 1) / (NWB * BB);
-  const int qt = blockIdx.x % qtiles;
-  const int bh = blockIdx.x / qtiles;
+  const int tq = blockIdx.x / (p.batch * p.heads_q);      // heavy (late) tiles first under the mask
+  const int bh = blockIdx.x % (p.batch * p.heads_q);
+  const int qt = CAUSAL ? qtiles - 1 - tq : tq;
   const int hq = bh % p.heads_q, b = bh / p.heads_q;
   const int kvh = hq / p.group;
   const int nq = p.seqlen_q, nk = p.seqlen_k;
@@ -236,8 +274,12 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dq_kernel(const BwdParams p) {
 
   const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
   bf16x8 qf[KS], gf[KS];
-  load_rowfrags<D>(qf, reinterpret_cast<const __bf16*>(p.q) + qo, p.q_stride[2], row, nq, lane);
-  load_rowfrags<D>(gf, reinterpret_cast<const __bf16*>(p.dout) + qo, p.q_stride[2], row, nq, lane);
+#pragma unroll
+  for (int kc = 0; kc < KS; ++kc) {
+    const int64_t e = (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half;
+    qf[kc] = as_bf16x8(row < nq ? load16(reinterpret_cast<const __bf16*>(p.q) + qo + e) : u32x4{0, 0, 0, 0});
+    gf[kc] = as_bf16x8(row < nq ? load16(reinterpret_cast<const __bf16*>(p.dout) + qo + e) : u32x4{0, 0, 0, 0});
+  }
   const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
   const float lse2 = row < nq ? p.lse[so + row] * kLog2e : __builtin_huge_valf();
   const float dsum = row < nq ? p.dsum[so + row] : 0.f;
@@ -250,33 +292,47 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dq_kernel(const BwdParams p) {
 
   const float c2 = p.scale_log2;
   const int k_end = CAUSAL ? min(nk, q0 + NWB * BB) : nk;
-  for (int kv0 = 0; kv0 < k_end; kv0 += BB) {
+  Prefetch<D, KB2> pk, pv;
+  if (0 < k_end) {
+    pk.load(kp, p.kv_stride[2], 0, nk, tid);
+    pv.load(vp, p.kv_stride[2], 0, nk, tid);
+  }
+  for (int kv0 = 0; kv0 < k_end; kv0 += KB2) {
     __syncthreads();
-    stage<D>(ks, kp, p.kv_stride[2], kv0, nk, tid);
-    stage<D>(vs, vp, p.kv_stride[2], kv0, nk, tid);
+    pk.store(ks, tid);
+    pv.store(vs, tid);
     __syncthreads();
-    if (CAUSAL && kv0 > rw0 + BB - 1) continue;    // these keys are in the future of every row of the wave
-
-    // S^T and dP^T for (keys, rows): register j holds key acc_key(j, half), row = lane % 32
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < KS; ++kc) {
-      s = mfma32(frag_sigma<D>(ks, lane, kc), qf[kc], s);
-      dp = mfma32(frag_sigma<D>(vs, lane, kc), gf[kc], dp);
+    if (kv0 + KB2 < k_end) {                 // in flight during this block's matrix work
+      pk.load(kp, p.kv_stride[2], kv0 + KB2, nk, tid);
+      pv.load(vp, p.kv_stride[2], kv0 + KB2, nk, tid);
     }
-    bf16x8 sb[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = kv0 + acc_key(j, half);
-      const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
-      const float pr = vis ? fast_exp2(fmaf(s[j], c2, -lse2)) : 0.f;
-      sb[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dsum));
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb0 = kv0 + sb * BB;
+      if (CAUSAL && kb0 > rw0 + BB - 1) continue;   // these keys are in the future of every row of the wave
+      const __bf16* kt = ks + sb * BB * D;
+      const __bf16* vt = vs + sb * BB * D;
+      // S^T and dP^T for (keys, rows): register j holds key acc_key(j, half), row = lane % 32
+      f32x16 sa = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KS; ++kc) {
+        sa = mfma32(frag_sigma<D>(kt, lane, kc), qf[kc], sa);
+        dp = mfma32(frag_sigma<D>(vt, lane, kc), gf[kc], dp);
+      }
+      bf16x8 sbf[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kb0 + acc_key(j, half);
+        const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
+        const float pr = vis ? fast_exp2(fmaf(sa[j], c2, -lse2)) : 0.f;
+        sbf[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dsum));
+      }
+      // dQ^T += K^T dS^T (keys are the contraction)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dq[db] = mfma32(frag_trans<D>(kt, lane, db, c), sbf[c], dq[db]);
     }
-    // dQ^T += K^T dS^T (keys are the contraction)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dq[db] = mfma32(frag_trans<D>(ks, lane, db, c), sb[c], dq[db]);
   }
   if (row < nq) {
     const int64_t o = (int64_t)b * p.dq_stride[0] + (int64_t)hq * p.dq_stride[1] + (int64_t)row * p.dq_stride[2];
@@ -296,7 +352,8 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t kwg = (int64_t)p.batch * p.heads_kv * ((p.seqlen_k + NWB * BB - 1) / (NWB * BB));
+  const int64_t ktiles = (p.seqlen_k + NWB * BB - 1) / (NWB * BB);
+  const int64_t kwg = (int64_t)p.batch * p.heads_kv * (CAUSAL ? (ktiles + 1) / 2 : ktiles);
   hipLaunchKernelGGL((detail::bwd_dkdv_kernel<D, CAUSAL, TOut>), dim3((unsigned)kwg), dim3(NWB * 64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -76,3 +76,10 @@ def test_window_flops_counts_visible_pairs():
 def test_varlen_flops_sums_sequences():
     assert cm.varlen_flops([3, 0, 5], 2, 4, False) == 4.0 * 2 * 4 * (9 + 25)
     assert cm.varlen_flops([3, 5], 2, 4, True) == 4.0 * 2 * 4 * (9 + 25) / 2
+
+
+def test_backward_flops_are_five_matmuls():
+    fwd = cm.attention_flops(1, 64, 8192, 8192, 128, True)
+    assert cm.backward_flops(1, 64, 8192, 8192, 128, True) == fwd * 5 / 2
+    # one (row, key) pair, d = 1: five products of 2 FLOPs each
+    assert cm.backward_flops(1, 1, 1, 1, 1, False) == 10.0
