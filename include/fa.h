@@ -249,7 +249,11 @@ FA_API size_t fa_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seq
  * of a kv head sum the contributions of its query heads. No atomics: the
  * result is deterministic.
  *
- * q, o, dout  [batch, heads_q, seqlen_q, head_dim] bf16, strides q_stride = {b, h, n}
+ * q, dout    [batch, heads_q, seqlen_q, head_dim] bf16, strides q_stride = {b, h, n}
+ * o           the same shape and element strides, o_dtype: BF16 or FP32. D is
+ *             computed from o as given; with a peaked softmax dP - D cancels,
+ *             so an FP32 o (fa_fwd with out_dtype FP32) gives visibly more
+ *             accurate dq and dk than the bf16-rounded one.
  * k, v        [batch, heads_kv, seqlen_k, head_dim] bf16, strides kv_stride
  * lse         [batch, heads_q, seqlen_q] float32, contiguous, as fa_fwd wrote it
  *             (with the same q, k, v, mask and softmax_scale; o is fa_fwd's output)
@@ -269,8 +273,8 @@ FA_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
                           int32_t heads_kv, int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
                           const int64_t q_stride[3], const int64_t kv_stride[3], const int64_t dq_stride[3],
-                          const int64_t dkv_stride[3], fa_dtype_t grad_dtype, fa_mask_t mask, float softmax_scale,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const int64_t dkv_stride[3], fa_dtype_t o_dtype, fa_dtype_t grad_dtype, fa_mask_t mask,
+                          float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. Never NULL. */
 FA_API const char* fa_status_string(fa_status_t status);

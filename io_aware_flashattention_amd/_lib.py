@@ -56,8 +56,8 @@ def load():
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,     # q k v o dout lse dq dk dv
                            _i32, _i32, _i32, _i32, _i32, _i32,              # batch Hq Hkv Nq Nk d
-                           _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                           _vp, ctypes.c_size_t, _vp]
+                           _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_float, _vp, ctypes.c_size_t, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
     lib.fa_decode.restype = ctypes.c_int
@@ -178,14 +178,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
         lse: torch.Tensor, causal: bool = False, scale: float | None = None,
         grad_dtype: torch.dtype | None = None, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
         dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Backward of ``fwd``. q, o, dout [B,Hq,N,d] bf16 sharing strides; k, v [B,Hkv,Nk,d] bf16
-    sharing strides; lse float32 [B,Hq,N] from ``fwd``. Returns (dq, dk, dv)."""
+    """Backward of ``fwd``. q, dout [B,Hq,N,d] bf16 and o (bf16 or float32) sharing element strides;
+    k, v [B,Hkv,Nk,d] bf16 sharing strides; lse float32 [B,Hq,N] from ``fwd``. Returns (dq, dk, dv)."""
     lib = load()
     B, Hq, N, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    for t in (q, k, v, o, dout):
+    for t in (q, k, v, dout):
         if t.dtype != torch.bfloat16:
-            raise ValueError("q, k, v, o and dout must be bfloat16")
+            raise ValueError("q, k, v and dout must be bfloat16")
     if o.stride() != q.stride() or dout.stride() != q.stride() or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("o and dout must share q's shape and strides")
     if v.stride() != k.stride() or v.shape != k.shape:
@@ -205,7 +205,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, Nk, d, _strides3(q), _strides3(k),
-                    _strides3(dq), _strides3(dk), _dtype_code(dq.dtype),
+                    _strides3(dq), _strides3(dk), _dtype_code(o.dtype), _dtype_code(dq.dtype),
                     FA_MASK_CAUSAL if causal else FA_MASK_NONE, float(scale), workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st)

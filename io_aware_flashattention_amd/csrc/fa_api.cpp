@@ -118,8 +118,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q, int32_t heads_kv,
                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[3],
                    const int64_t kv_stride[3], const int64_t dq_stride[3], const int64_t dkv_stride[3],
-                   fa_dtype_t grad_dtype, fa_mask_t mask, float softmax_scale, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   fa_dtype_t o_dtype, fa_dtype_t grad_dtype, fa_mask_t mask, float softmax_scale,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: tensor pointers must be non-null");
   if (!q_stride || !kv_stride || !dq_stride || !dkv_stride)
@@ -131,6 +131,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                 (double)softmax_scale);
   if (grad_dtype != FA_DTYPE_BF16 && grad_dtype != FA_DTYPE_FP32)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: unknown grad_dtype %d", (int)grad_dtype);
+  if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: unknown o_dtype %d", (int)o_dtype);
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd: unknown mask %d", (int)mask);
   for (int i = 0; i < 3; ++i)
@@ -159,7 +161,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   const int64_t gb = grad_dtype == FA_DTYPE_BF16 ? 2 : 4;
   uintptr_t lo[10], hi[10];
   span(q, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[0], &hi[0]);
-  span(o, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[1], &hi[1]);
+  span(o, q_stride, batch, heads_q, seqlen_q, head_dim, o_dtype == FA_DTYPE_FP32 ? 4 : 2, &lo[1], &hi[1]);
   span(dout, q_stride, batch, heads_q, seqlen_q, head_dim, 2, &lo[2], &hi[2]);
   span(k, kv_stride, batch, heads_kv, seqlen_k, head_dim, 2, &lo[3], &hi[3]);
   span(v, kv_stride, batch, heads_kv, seqlen_k, head_dim, 2, &lo[4], &hi[4]);
@@ -192,6 +194,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = mask == FA_MASK_CAUSAL;
   p.grad_fp32 = grad_dtype == FA_DTYPE_FP32;
+  p.o_fp32 = o_dtype == FA_DTYPE_FP32;
   hipError_t e = fa::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(e));
   return ok();

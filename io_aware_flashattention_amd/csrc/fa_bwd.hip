@@ -131,10 +131,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
     const int64_t bh = row / p.seqlen_q;
     const int h = (int)(bh % p.heads_q), b = (int)(bh / p.heads_q);
     const int64_t off = (int64_t)b * p.q_stride[0] + (int64_t)h * p.q_stride[1] + (int64_t)i * p.q_stride[2] + 8 * c;
-    const bf16x8 o = as_bf16x8(load16(reinterpret_cast<const __bf16*>(p.o) + off));
     const bf16x8 g = as_bf16x8(load16(reinterpret_cast<const __bf16*>(p.dout) + off));
+    if (p.o_fp32) {
+      const float* op = reinterpret_cast<const float*>(p.o) + off;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(op), c4 = *reinterpret_cast<const f32x4*>(op + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = fmaf((float)o[e], (float)g[e], s);
+      for (int e = 0; e < 4; ++e) s = fmaf(a[e], (float)g[e], s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fmaf(c4[e], (float)g[4 + e], s);
+    } else {
+      const bf16x8 o = as_bf16x8(load16(reinterpret_cast<const __bf16*>(p.o) + off));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf((float)o[e], (float)g[e], s);
+    }
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) s += __shfl_xor(s, w, LPR);

@@ -51,7 +51,7 @@ struct BwdParams {
   const void* q;       // [B, Hq, Nq, d] bf16, strides q_stride (shared by o, dout)
   const void* k;       // [B, Hkv, Nk, d] bf16, strides kv_stride (shared by v)
   const void* v;
-  const void* o;
+  const void* o;       // bf16 or float32 (o_fp32), q_stride in its own elements
   const void* dout;
   const float* lse;    // [B, Hq, Nq] natural log, from the forward pass
   float* dsum;         // workspace [B, Hq, Nq]: rowsum(dO * O)
@@ -61,7 +61,7 @@ struct BwdParams {
   int64_t q_stride[3], kv_stride[3], dq_stride[3], dkv_stride[3];
   int batch, heads_q, heads_kv, group, seqlen_q, seqlen_k, head_dim;
   float scale, scale_log2;
-  bool causal, grad_fp32;
+  bool causal, grad_fp32, o_fp32;
 };
 
 // n_qtiles is filled in by the launchers (it depends on the kernel's row tile).

@@ -119,13 +119,13 @@ def _bwd(**kw):
     a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, do=FAKE + 0x400000,
              lse=FAKE + 0x500000, dq=FAKE + 0x600000, dk=FAKE + 0x700000, dv=FAKE + 0x800000, B=1, Hq=4, Hkv=2,
              Nq=64, Nk=64, d=128, qs=(4 * 64 * 128, 64 * 128, 128), ks=(2 * 64 * 128, 64 * 128, 128),
-             dqs=(4 * 64 * 128, 64 * 128, 128), dks=(2 * 64 * 128, 64 * 128, 128), gd=1, mask=1, scale=0.125,
+             dqs=(4 * 64 * 128, 64 * 128, 128), dks=(2 * 64 * 128, 64 * 128, 128), od=0, gd=1, mask=1, scale=0.125,
              ws=FAKE + 0x900000, wsb=1 << 20)
     a.update(kw)
     arr = lambda t: (ctypes.c_int64 * 3)(*t) if t is not None else None
     st = lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
                     a["Hkv"], a["Nq"], a["Nk"], a["d"], arr(a["qs"]), arr(a["ks"]), arr(a["dqs"]), arr(a["dks"]),
-                    a["gd"], a["mask"], a["scale"], a["ws"], a["wsb"], None)
+                    a["od"], a["gd"], a["mask"], a["scale"], a["ws"], a["wsb"], None)
     return st, lib.fa_last_error_message().decode()
 
 
@@ -134,6 +134,7 @@ def _bwd(**kw):
     (dict(dks=None), 1, "stride"),
     (dict(Nk=0), 1, "positive"),
     (dict(gd=5), 1, "grad_dtype"),
+    (dict(od=9), 1, "o_dtype"),
     (dict(mask=2), 1, "mask"),
     (dict(scale=float("nan")), 1, "softmax_scale"),
     (dict(d=32), 2, "head_dim"),

@@ -1,17 +1,20 @@
 """GPU parity of fa_bwd (through the C ABI) against the fp64 oracle's backward.
 
-The forward pass runs on the GPU first (its bf16 O and float32 LSE are what a
+The forward pass runs on the GPU first (its O and float32 LSE are what a
 training step would hand to the backward), then dQ, dK and dV are compared
 with attention_bwd_ref on the same bf16 inputs and dO.
 
 Bar (derived from the arithmetic, see the design notes): the kernels feed
 bf16-rounded P and dS (relative error <= 2^-9 each) to float32-accumulating
-matrix cores, and D = rowsum(dO * O) uses the bf16-rounded O. Each gradient
-element is a sum of such terms, so its error is bounded by about 2^-8 times
-the sum of the magnitudes of its terms; over whole tensors this stays below
-1% of the largest gradient element and 0.4% of the mean magnitude. The gate
-is max|err| <= 1e-2 * max|ref| and mean|err| <= 4e-3 * mean|ref| per tensor
-(normalisers floored at 1e-2 and 1e-3: a row with one visible key has dS = 0).
+matrix cores. Each gradient element is a sum of such terms, so its error is
+bounded by about 2^-8 times the sum of the magnitudes of its terms; over whole
+tensors this stays below 1% of the largest gradient element and 0.4% of the
+mean magnitude. The gate is max|err| <= 1e-2 * max|ref| and
+mean|err| <= 4e-3 * mean|ref| per tensor (normalisers floored at 1e-2 and
+1e-3: a row with one visible key has dS = 0), with the float32 O of the
+forward. With the bf16-rounded O, D = rowsum(dO * O) carries an error of
+about 2^-9 of its terms, and where one key dominates a row dP - D cancels and
+passes that error on to dS whole: that path has its own gate below.
 """
 import numpy as np
 import pytest
@@ -24,6 +27,7 @@ from tests.parity import say, to_dev
 pytestmark = pytest.mark.gpu
 
 MAX_REL, MEAN_REL = 1e-2, 4e-3
+MAX_REL_O16, MEAN_REL_O16 = 2e-2, 1.5e-2        # bf16 O (measured worst: 0.9% and 0.75%)
 
 
 def fa():
@@ -31,7 +35,7 @@ def fa():
     return m
 
 
-def check_grad(got, ref, what):
+def check_grad(got, ref, what, max_rel=MAX_REL, mean_rel=MEAN_REL):
     g = got.detach().float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(g)), f"{what}: non-finite"
     err = np.abs(g - ref)
@@ -39,15 +43,15 @@ def check_grad(got, ref, what):
     mx = err.max() / max(np.abs(ref).max(), 1e-2)
     mn = err.mean() / max(np.abs(ref).mean(), 1e-3)
     say(f"  {what}: max|err|/max|ref| {mx:.2e}  mean|err|/mean|ref| {mn:.2e}")
-    assert mx <= MAX_REL and mn <= MEAN_REL, f"{what}: {mx:.3e} {mn:.3e}"
+    assert mx <= max_rel and mn <= mean_rel, f"{what}: {mx:.3e} {mn:.3e}"
 
 
-def run_case(B, Hq, Hkv, N, d, causal, seed, grad_dtype=torch.float32):
-    q, k, v = W.make_random_prefill(B, Hq, Hkv, N, N, d, seed=seed)
+def run_case(B, Hq, Hkv, N, d, causal, seed, grad_dtype=torch.float32, o_dtype=torch.float32, heavy=0.0):
+    q, k, v = W.make_random_prefill(B, Hq, Hkv, N, N, d, seed=seed, heavy_frac=heavy)
     g, _, _ = W.make_random_prefill(B, Hq, Hkv, N, N, d, seed=seed + 1)      # dO
     qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
     scale = 1.0 / np.sqrt(d)
-    o, lse = fa().fwd(qd, kd, vd, causal=causal, scale=scale)
+    o, lse = fa().fwd(qd, kd, vd, causal=causal, scale=scale, out_dtype=o_dtype)
     dq, dk, dv = fa().bwd(qd, kd, vd, o, gd, lse, causal=causal, scale=scale, grad_dtype=grad_dtype)
     torch.cuda.synchronize()
     rq, rk, rv, _ = attention_bwd_ref(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(g), scale, causal=causal)
@@ -62,6 +66,18 @@ def test_bwd_small(d, causal, N):
     got, ref, _ = run_case(2, 4, 2, N, d, causal, seed=900 + N + d)
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         check_grad(a, b, f"{name} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
+def test_bwd_heavy_keys(d, o_dtype):
+    """1% of K rows x8, as in the long-context workload: peaked rows make dP - D
+    cancel, which is where the precision of O shows."""
+    say(f"case bwd heavy keys d={d} o={o_dtype}")
+    got, ref, _ = run_case(1, 8, 2, 777, d, True, seed=930 + d, o_dtype=o_dtype, heavy=0.01)
+    tol = (MAX_REL, MEAN_REL) if o_dtype == torch.float32 else (MAX_REL_O16, MEAN_REL_O16)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(a, b, f"{name} heavy d={d} o={o_dtype}", *tol)
 
 
 @pytest.mark.parametrize("causal", [False, True])
