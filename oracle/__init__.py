@@ -7,6 +7,8 @@ from .attention import (attention_bwd_ref, attention_ref, block_summary, decode_
                         merge_summaries, paged_decode_ref, paged_rows, split_decode_ref,
                         stream_attention, varlen_ref)
 
-__all__ = ["attention_ref", "attention_bwd_ref", "stream_attention", "block_summary", "merge_summaries",
+from .fp8 import e4m3_round, fp8_attention_ref, hadamard, quantize, rotate_f32
+
+__all__ = ["e4m3_round", "hadamard", "rotate_f32", "quantize", "fp8_attention_ref", "attention_ref", "attention_bwd_ref", "stream_attention", "block_summary", "merge_summaries",
            "merge_lse", "decode_ref", "split_decode_ref", "paged_rows", "paged_decode_ref",
            "varlen_ref"]
