@@ -7,13 +7,15 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
      kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
      and merge kernel).
-After the timed steps, four more paths are timed on their own (not part of
+After the timed steps, five more paths are timed on their own (not part of
 the step): the same decode against a paged cache (fa_decode_paged: 16-token
 pages in a token-major pool, shuffled block table) as ``decode_paged``, and
 through fa_fwd_varlen the 8192-token sliding-window-1024 prefill
 (``prefill_window``) and a packed batch of 16 causal sequences of 1..8192
 tokens (``prefill_varlen``), and the backward of the step's prefill through
-fa_bwd (``backward``, 2.5x the forward FLOPs).
+fa_bwd (``backward``, 2.5x the forward FLOPs), and the FP8 prefill of the
+step's workload (``prefill_fp8``: fa_fwd_fp8, with fa_fp8_quantize timed
+apart).
 Inputs are generated and uploaded before the timed region. W untimed warmup
 steps, then exactly K timed steps between two device synchronisations. Kernel
 durations come from HIP events recorded on the stream the kernels run on.
@@ -46,6 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 matrix peak (twice bf16)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 PREFILL_CFG = "c4a_gqa_8k"
 DECODE_CFG = "c5_decode"
@@ -194,6 +197,20 @@ def run(args):
                                   + (f"causal window {win}" if win is not None else "causal"),
                       "kernel": "fa_fwd_varlen"}
         del vq, vk, vv, vo
+    # FP8 prefill of the step's workload: quantiser and attention timed separately
+    signs = torch.from_numpy(np.random.default_rng([pc.seed, 7]).choice([-1.0, 1.0], pc.head_dim)
+                             .astype(np.float32)).to(dev)
+    quant = fa.fp8_quantize(q, k, v, signs)
+    o8 = torch.empty_like(q)
+    ms_q = time_launches(lambda: fa.fp8_quantize(q, k, v, signs))
+    ms_a = time_launches(lambda: fa.fwd_fp8(quant, causal=True, scale=pc.scale, out=o8, lse=lse))
+    fl = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)
+    extra["prefill_fp8"] = {"ms": round(ms_a, 4), "value": round(fl / (ms_a * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                            "frac_fp8_peak": round(fl / (ms_a * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                            "quantize_ms": round(ms_q, 4), "flops_per_launch": fl,
+                            "workload": "causal GQA B1 Hq64 Hkv8 N8192 d128, e4m3 with random-sign Hadamard",
+                            "kernel": "fa_fwd_fp8 (fa_fp8_quantize timed apart)"}
+    del quant, o8
     # backward of the step's prefill (same inputs, its O and LSE, a seeded dO)
     gh, _, _ = W.make_random_prefill(pc.batch, pc.heads_q, pc.heads_kv, pc.seqlen, pc.seqlen, pc.head_dim,
                                      seed=pc.seed + 100)
@@ -322,8 +339,9 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
     """Label per-dispatch rows (sorted by Dispatch_Id) with the bench phase
     they belong to. The bench launches, in this order: n_launch steps of
     (prefill, decode split, decode merge); n_launch paged decodes (paged split,
-    merge); n_launch window prefills; n_launch packed prefills; one prefill
-    for the backward's inputs, then n_launch backward passes. The prefill
+    merge); n_launch window prefills; n_launch packed prefills; the fp8
+    quantiser and prefill (their own kernels); one prefill for the backward's
+    inputs, then n_launch backward passes. The prefill
     kernel is the same instantiation in every prefill phase, so the phase
     comes from the dispatch order."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
@@ -331,7 +349,9 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
     out = []
     for r in rows:
         name = r.get(name_key, "")
-        if re.search(r"fwd_\w*kernel", name):
+        if "fp8" in name:
+            label = "fp8 " + re.sub(r".*((?:fwd|fp8)_\w*?_kernel).*", r"\1", name)
+        elif re.search(r"fwd_\w*kernel", name):
             i = seen["fwd"]
             seen["fwd"] += 1
             label = ("prefill c4a (step)", "prefill window c7", "prefill varlen c6",

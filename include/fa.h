@@ -21,6 +21,8 @@
  *   fa_bwd     gradients of fa_fwd with respect to q, k and v, recomputing the
  *              probabilities from the saved log-sum-exp.
  *
+ *   fa_fp8_quantize, fa_fwd_fp8  FP8 (e4m3) prefill with incoherent processing.
+ *
  *   fa_decode  single-token decode against a KV cache, with the key axis split
  *              across workgroups; every split writes a partial output and its
  *              log-sum-exp, and a second small kernel merges the partials
@@ -275,6 +277,59 @@ FA_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const voi
                           const int64_t q_stride[3], const int64_t kv_stride[3], const int64_t dq_stride[3],
                           const int64_t dkv_stride[3], fa_dtype_t o_dtype, fa_dtype_t grad_dtype, fa_mask_t mask,
                           float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fp8_quantize -- the quantiser of the FP8 path ("FlashAttention Explained:
+ * IO-Aware Attention, Tiling, Online Softmax and FP8 on Hopper", section "FP8
+ * Attention and Incoherent Processing"). Q and K rows are multiplied by the
+ * same orthogonal matrix diag(signs) H / sqrt(128) (H the Sylvester Hadamard
+ * matrix; a fast Walsh-Hadamard transform in float32), which leaves Q K^T
+ * unchanged, then stored as OCP e4m3 (largest finite 448, nearest-even) with
+ * one float32 scale per block: codes = e4m3(x * 448 / amax), scale =
+ * amax / 448 (1 for an all-zero block). V is not rotated; it gets one scale
+ * per kv head.
+ *
+ * q       [batch, heads_q, seqlen, 128] bf16, strides q_stride = {b, h, n}
+ * k, v    [batch, heads_kv, seqlen, 128] bf16, strides kv_stride
+ * signs   DEVICE float [128] of +1/-1 drawn by the caller, or NULL for no
+ *         rotation (plain block quantisation)
+ * outputs (contiguous, caller-owned):
+ *   q8       [batch, heads_q, seqlen, 128] e4m3 bytes
+ *   q_scale  [batch, heads_q, ceil(seqlen / 128)] float32 (one per 128 rows)
+ *   k8       [batch, heads_kv, seqlen, 128] e4m3 bytes
+ *   k_scale  [batch, heads_kv, ceil(seqlen / 64)] float32 (one per 64 keys)
+ *   v8t      [batch, heads_kv, 128, npad] e4m3 bytes, npad = 64 ceil(seqlen / 64):
+ *            V transposed; inside every 64-key tile key kappa sits at position
+ *            32 ((kappa / 4) % 2) + 16 (kappa / 32) + 4 ((kappa % 32) / 8) + kappa % 4;
+ *            padding keys are zero
+ *   v_scale  [batch, heads_kv] float32
+ * Supported: head_dim 128; heads_q % heads_kv == 0; 16-byte aligned tensors;
+ * strides multiples of 8 elements. Otherwise FA_ERR_UNSUPPORTED.
+ */
+FA_API fa_status_t fa_fp8_quantize(const void* q, const void* k, const void* v, const float* signs,
+                                   int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen,
+                                   int32_t head_dim, const int64_t q_stride[3], const int64_t kv_stride[3],
+                                   void* q8, void* k8, void* v8t, float* q_scale, float* k_scale, float* v_scale,
+                                   void* stream);
+
+/*
+ * fa_fwd_fp8 -- prefill attention on fa_fp8_quantize's outputs: both products
+ * on the e4m3 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), the softmax in
+ * float32. The probabilities are quantised too, as e4m3(2^8 * 2^(x - m)) with
+ * x the scaled score in base 2 and m an integer base at or above the row's
+ * running maximum; O is divided by the sum of the quantised weights; the LSE
+ * is the float32 log-sum-exp of the dequantised scores. FP8 changes numerics:
+ * results differ from fa_fwd by the quantisation error (about 1% mean on O).
+ *
+ * o    [batch, heads_q, seqlen, 128] out_dtype (BF16 or FP32), contiguous
+ * lse  [batch, heads_q, seqlen] float32, contiguous; may be NULL
+ * mask FA_MASK_NONE or FA_MASK_CAUSAL
+ * Supported: head_dim 128; heads_q % heads_kv == 0; 16-byte aligned tensors.
+ */
+FA_API fa_status_t fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
+                              const float* k_scale, const float* v_scale, void* o, float* lse, int32_t batch,
+                              int32_t heads_q, int32_t heads_kv, int32_t seqlen, int32_t head_dim,
+                              fa_dtype_t out_dtype, fa_mask_t mask, float softmax_scale, void* stream);
 
 /* Static description of a status code. Never NULL. */
 FA_API const char* fa_status_string(fa_status_t status);

@@ -21,8 +21,8 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd_workspace_bytes", "fa_bwd", "fa_decode_workspace_bytes",
-            "fa_decode", "fa_decode_paged", "fa_status_string", "fa_last_error_message")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd_workspace_bytes", "fa_bwd", "fa_fp8_quantize", "fa_fwd_fp8",
+            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string", "fa_last_error_message")
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
 _lib = None
@@ -58,6 +58,12 @@ def load():
                            _i32, _i32, _i32, _i32, _i32, _i32,              # batch Hq Hkv Nq Nk d
                            _i64p, _i64p, _i64p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                            ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fp8_quantize.restype = ctypes.c_int
+    lib.fa_fp8_quantize.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p, _i64p,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
     lib.fa_decode.restype = ctypes.c_int
@@ -210,6 +216,59 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
                     workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st)
     return dq, dk, dv
+
+
+def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None = None) -> dict:
+    """FP8 quantiser. q [B,Hq,N,128], k/v [B,Hkv,N,128] bf16 (k and v sharing strides); signs a
+    float32 [128] tensor of +-1 on the GPU (None: no rotation). Returns the e4m3 tensors and scales."""
+    lib = load()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must be bfloat16")
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 vector of head_dim entries")
+    f8, dev = torch.float8_e4m3fn, q.device
+    npad = -(-N // 64) * 64
+    out = dict(q8=torch.empty((B, Hq, N, d), dtype=f8, device=dev),
+               q_scale=torch.empty((B, Hq, -(-N // 128)), dtype=torch.float32, device=dev),
+               k8=torch.empty((B, Hkv, N, d), dtype=f8, device=dev),
+               k_scale=torch.empty((B, Hkv, npad // 64), dtype=torch.float32, device=dev),
+               v8t=torch.empty((B, Hkv, d, npad), dtype=f8, device=dev),
+               v_scale=torch.empty((B, Hkv), dtype=torch.float32, device=dev))
+    st = lib.fa_fp8_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), signs.data_ptr() if signs is not None else None,
+                             B, Hq, Hkv, N, d, _strides3(q), _strides3(k), out["q8"].data_ptr(), out["k8"].data_ptr(),
+                             out["v8t"].data_ptr(), out["q_scale"].data_ptr(), out["k_scale"].data_ptr(),
+                             out["v_scale"].data_ptr(), _stream(q.device))
+    _check(st)
+    return out
+
+
+def fwd_fp8(quant: dict, causal: bool = False, scale: float | None = None, out_dtype: torch.dtype = torch.bfloat16,
+            out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+    """FP8 prefill on ``fp8_quantize``'s outputs. Returns (O [B,Hq,N,128], LSE float32 [B,Hq,N])."""
+    lib = load()
+    B, Hq, N, d = quant["q8"].shape
+    Hkv = quant["k8"].shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=quant["q8"].device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if lse is True:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=out.device)
+    elif lse is False:
+        lse = None
+    st = lib.fa_fwd_fp8(quant["q8"].data_ptr(), quant["k8"].data_ptr(), quant["v8t"].data_ptr(),
+                        quant["q_scale"].data_ptr(), quant["k_scale"].data_ptr(), quant["v_scale"].data_ptr(),
+                        out.data_ptr(), lse.data_ptr() if lse is not None else None, B, Hq, Hkv, N, d,
+                        _dtype_code(out.dtype), FA_MASK_CAUSAL if causal else FA_MASK_NONE, float(scale),
+                        _stream(out.device))
+    _check(st)
+    return out, lse
 
 
 def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seqlen: int, head_dim: int) -> int:

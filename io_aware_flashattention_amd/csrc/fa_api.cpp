@@ -200,6 +200,72 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   return ok();
 }
 
+fa_status_t fa_fp8_quantize(const void* q, const void* k, const void* v, const float* signs,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen, int32_t head_dim,
+                            const int64_t q_stride[3], const int64_t kv_stride[3], void* q8, void* k8, void* v8t,
+                            float* q_scale, float* k_scale, float* v_scale, void* stream) {
+  if (!q || !k || !v || !q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fp8_quantize: tensor pointers must be non-null (signs may be NULL)");
+  if (!q_stride || !kv_stride) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fp8_quantize: stride arrays must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || seqlen <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fp8_quantize: sizes must be positive");
+  for (int i = 0; i < 3; ++i)
+    if (q_stride[i] < 0 || kv_stride[i] < 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_fp8_quantize: strides must be non-negative");
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fp8_quantize: head_dim %d not supported (128)", head_dim);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fp8_quantize: heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fp8_quantize: tensors must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (q_stride[i] % 8 || kv_stride[i] % 8)
+      return fail(FA_ERR_UNSUPPORTED, "fa_fp8_quantize: strides must be multiples of 8 elements");
+  if (heads_q > 65535 || heads_kv > 65535 || batch > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fp8_quantize: problem too large for one launch");
+  fa::Fp8QuantParams p{};
+  p.q = q; p.k = k; p.v = v; p.signs = signs;
+  p.q8 = q8; p.k8 = k8; p.v8t = v8t; p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  for (int i = 0; i < 3; ++i) { p.q_stride[i] = q_stride[i]; p.kv_stride[i] = kv_stride[i]; }
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.seqlen = seqlen;
+  hipError_t e = fa::launch_fp8_quant(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fp8_quantize: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status_t fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale, const float* k_scale,
+                       const float* v_scale, void* o, float* lse, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                       int32_t seqlen, int32_t head_dim, fa_dtype_t out_dtype, fa_mask_t mask, float softmax_scale,
+                       void* stream) {
+  if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_fp8: tensor pointers must be non-null");
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || seqlen <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_fp8: sizes must be positive");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_fp8: softmax_scale must be finite and positive (got %g)",
+                (double)softmax_scale);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_fp8: unknown out_dtype %d", (int)out_dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_fp8: unknown mask %d", (int)mask);
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: head_dim %d not supported (128)", head_dim);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: tensors must be 16-byte aligned");
+  if ((int64_t)batch * heads_q * ((seqlen + 127) / 128) > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: problem too large for one launch");
+  fa::Fp8FwdParams p{};
+  p.q8 = q8; p.k8 = k8; p.v8t = v8t; p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.o = o; p.lse = lse;
+  p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv; p.seqlen = seqlen;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = mask == FA_MASK_CAUSAL;
+  p.out_fp32 = out_dtype == FA_DTYPE_FP32;
+  hipError_t e = fa::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_fp8: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fa_status_string(fa_status_t s) {
   switch (s) {
     case FA_OK: return "FA_OK";

@@ -1,0 +1,395 @@
+// FP8 (e4m3) prefill with incoherent processing, for head_dim 128 on gfx950
+// ("FlashAttention Explained: IO-Aware Attention, Tiling, Online Softmax and
+// FP8 on Hopper", section "FP8 Attention and Incoherent Processing").
+//
+// Quantiser. Q and K rows are multiplied by diag(s) H / sqrt(128) (random
+// signs s, Sylvester Hadamard H; a fast Walsh-Hadamard transform: sixteen
+// lanes hold a row, eight values each, butterflies of distance 1, 2, 4 inside
+// a lane and 8 .. 64 across lanes by shuffles) and quantised to OCP e4m3 with
+// one float32 scale per block of rows (128 query rows, 64 keys): codes =
+// e4m3(x * 448 / amax), scale = amax / 448. V keeps its values and gets one
+// scale per kv head; it is stored transposed, [d][key], with the keys of each
+// 64-key tile permuted into the order in which one lane of the attention
+// kernel holds its row's probabilities, so the P V operand is two 16-byte
+// reads.
+//
+// Attention. The tile loop of the bf16 kernels on v_mfma_scale_f32_32x32x64
+// _f8f6f4 (block scales fixed at 1): S^T = K Q^T for 64-key tiles as two
+// 32-key blocks of two k-steps, the softmax in float32 with the tile's
+// q-scale x k-scale folded into the one FMA per score, and O^T += V^T P^T
+// with P quantised to e4m3 as 2^8 * 2^(x - m) against an integer base m that
+// moves with the row maximum (so every rescale is an exact power of two and
+// every weight keeps three mantissa bits down to 2^-14 of the largest). O is
+// divided by the sum of the quantised weights (one more MFMA against a row of
+// ones) and multiplied by V's scale; the LSE uses the float32 sum.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int D8 = 128;      // head dim
+constexpr int QB = 128;      // query rows per scale block (and per attention workgroup)
+constexpr int KT = 64;       // keys per scale block and per tile
+constexpr int ST8 = 3;       // K/V tile ring depth
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void8;
+// per-tile scales are read at wave-uniform addresses through the constant
+// address space (scalar loads), so they never wait on the DMA's counter
+typedef __attribute__((address_space(4))) const float const_f32;
+
+// two floats (already within +-448) to e4m3 bytes in the low or high half of w
+template <bool HI>
+__device__ __forceinline__ int pack2(float a, float b, int w) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, HI);
+}
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+
+// position of key kappa (0..63) of a tile in the transposed V storage: the
+// attention kernel's lane of half h holds, in byte b, the probability of key
+// 8(b%16/4) + 4h + b%4 + 32(b/16); the storage puts that key at 32h + b
+__device__ __forceinline__ int vpos(int kappa) {
+  const int blk = kappa >> 5, r = kappa & 31;
+  const int h = (r >> 2) & 1, bb = ((r >> 3) << 2) | (r & 3);
+  return 32 * h + 16 * blk + bb;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) x = fmaxf(x, __shfl_xor(x, w, 64));
+  return x;
+}
+
+}  // namespace
+
+namespace detail {
+
+// Rotate and quantise one block of ROWS rows of Q or K: grid (blocks, heads, batch).
+template <int ROWS>
+__global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const Fp8QuantParams p, int which) {
+  constexpr int PASSES = ROWS / 16;          // 16 rows per pass, 16 lanes per row
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 15, rsub = tid >> 4;   // lane's 8-value chunk, row within the pass
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = p.seqlen;
+  const __bf16* src = reinterpret_cast<const __bf16*>(which == 0 ? p.q : p.k);
+  const int64_t* st = which == 0 ? p.q_stride : p.kv_stride;
+  const int heads = which == 0 ? p.heads_q : p.heads_kv;
+  src += (int64_t)b * st[0] + (int64_t)h * st[1];
+
+  float sg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sg[e] = p.signs != nullptr ? p.signs[8 * c + e] : 1.f;
+  const float inv_sqrt_d = 0.08838834764831845f;
+
+  float x[PASSES][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = blk * ROWS + ps * 16 + rsub;
+    const bool ok = row < n;
+    const bf16x8 v = as_bf16x8(ok ? load16(src + (int64_t)row * st[2] + 8 * c) : u32x4{0, 0, 0, 0});
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * sg[e];
+    if (p.signs != nullptr) {
+      // butterflies inside the lane: distance 1, 2, 4
+#pragma unroll
+      for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((e & hh) == 0) {
+            const float a = y[e], bb = y[e + hh];
+            y[e] = a + bb;
+            y[e + hh] = a - bb;
+          }
+      // across lanes: distance 8, 16, 32, 64 = lane distance 1, 2, 4, 8
+#pragma unroll
+      for (int lh = 1; lh < 16; lh <<= 1) {
+        const bool upper = (c & lh) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float other = __shfl_xor(y[e], lh, 64);
+          y[e] = upper ? other - y[e] : y[e] + other;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= inv_sqrt_d;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[ps][e] = ok ? y[e] : 0.f;
+      amax = fmaxf(amax, fabsf(x[ps][e]));
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float safe = amax > 0.f ? amax : 448.f;
+  const float inv = 448.f / safe;
+  float* scale = which == 0 ? p.q_scale : p.k_scale;
+  const int nblk = (n + ROWS - 1) / ROWS;
+  if (tid == 0) scale[((int64_t)b * heads + h) * nblk + blk] = safe / 448.f;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(which == 0 ? p.q8 : p.k8) + ((int64_t)b * heads + h) * n * D8;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = blk * ROWS + ps * 16 + rsub;
+    if (row >= n) continue;
+    int w0 = pack2<false>(clamp448(x[ps][0] * inv), clamp448(x[ps][1] * inv), 0);
+    w0 = pack2<true>(clamp448(x[ps][2] * inv), clamp448(x[ps][3] * inv), w0);
+    int w1 = pack2<false>(clamp448(x[ps][4] * inv), clamp448(x[ps][5] * inv), 0);
+    w1 = pack2<true>(clamp448(x[ps][6] * inv), clamp448(x[ps][7] * inv), w1);
+    *reinterpret_cast<u32x2*>(dst + (int64_t)row * D8 + 8 * c) = u32x2{(uint32_t)w0, (uint32_t)w1};
+  }
+}
+
+// Quantise one kv head of V (one scale) into the transposed, key-permuted
+// layout: grid (heads_kv, batch).
+__global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p) {
+  __shared__ float wmax[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D8 * KT];     // [d][position]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
+  const __bf16* src = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride[0] + (int64_t)h * p.kv_stride[1];
+  const int c = tid & 15, rsub = tid >> 4;   // 16 lanes per row, 8 values each
+
+  float amax = 0.f;
+  for (int row = rsub; row < n; row += 16) {
+    const bf16x8 v = as_bf16x8(load16(src + (int64_t)row * p.kv_stride[2] + 8 * c));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+  }
+  amax = wave_max(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float safe = amax > 0.f ? amax : 448.f;
+  const float inv = 448.f / safe;
+  if (tid == 0) p.v_scale[(int64_t)b * p.heads_kv + h] = safe / 448.f;
+
+  uint8_t* dst = reinterpret_cast<uint8_t*>(p.v8t) + ((int64_t)b * p.heads_kv + h) * D8 * npad;
+  for (int t0 = 0; t0 < npad; t0 += KT) {
+    __syncthreads();                         // the previous tile's readers are done
+#pragma unroll
+    for (int ps = 0; ps < KT / 16; ++ps) {
+      const int kappa = ps * 16 + rsub, row = t0 + kappa;
+      const bf16x8 v = as_bf16x8(row < n ? load16(src + (int64_t)row * p.kv_stride[2] + 8 * c) : u32x4{0, 0, 0, 0});
+      const int pos = vpos(kappa);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int w = pack2<false>(clamp448((float)v[e] * inv), clamp448((float)v[e + 1] * inv), 0);
+        tile[(8 * c + e) * KT + pos] = (uint8_t)(w & 0xff);
+        tile[(8 * c + e + 1) * KT + pos] = (uint8_t)((w >> 8) & 0xff);
+      }
+    }
+    __syncthreads();
+    // 128 rows x 64 bytes out: 16 bytes per thread, two rounds
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, d = idx >> 2, ch = idx & 3;
+      *reinterpret_cast<u32x4*>(dst + (int64_t)d * npad + t0 + 16 * ch) =
+          *reinterpret_cast<const u32x4*>(tile + d * KT + 16 * ch);
+    }
+  }
+}
+
+// Attention on the quantised operands: 4 waves x 32 query rows per workgroup.
+template <bool CAUSAL, typename TOut>
+__global__ __launch_bounds__(256) void fwd_fp8_kernel(const Fp8FwdParams p) {
+  constexpr int NW = 4, BRW = 32 * NW, TILEB = KT * D8;   // bytes per K (or V^T) tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST8 * 2 * TILEB];  // [stage][K, V^T][8 KB]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
+  const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
+  const int nqt = (n + BRW - 1) / BRW;
+  const int t = blockIdx.x % nqt;
+  const int bh = blockIdx.x / nqt;
+  const int hq = bh % p.heads_q, b = bh / p.heads_q;
+  const int kvh = hq / p.group;
+  const int qt = CAUSAL ? nqt - 1 - t : t;   // heavy tiles first
+  const int q0 = qt * BRW, wrow0 = q0 + wave * 32, row = wrow0 + r32;
+  const int kv_end = CAUSAL ? min(n, q0 + BRW) : n;
+  const int ntiles = (kv_end + KT - 1) / KT;
+  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / KT + 1) : ntiles;
+
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k8) + ((int64_t)b * p.heads_kv + kvh) * n * D8;
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v8t) + ((int64_t)b * p.heads_kv + kvh) * D8 * npad;
+  const const_f32* ksc = (const const_f32*)p.k_scale + ((int64_t)b * p.heads_kv + kvh) * (npad / KT);
+  const float qs = p.q_scale[((int64_t)b * p.heads_q + hq) * ((n + QB - 1) / QB) + q0 / QB];
+  const float vs = p.v_scale[(int64_t)b * p.heads_kv + kvh];
+
+  // DMA: a tile is 8 K writes and 8 V^T writes of 1 KB; wave w issues two of each.
+  // K: write i covers rows 8i..8i+7 (16-byte chunk lane%8 of row 8i + lane/8);
+  // V^T: write i covers d rows 16i..16i+15 (chunk lane%4 of row 16i + lane/4).
+  // The global chunk is XOR-swizzled by the row, so reads below XOR back.
+  auto issue = [&](int tile, int stg) {
+    const int kv0 = tile * KT;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int i = 2 * wave + i2;
+      const int kr = 8 * i + (lane >> 3), kc = lane & 7;
+      const int key = min(kv0 + kr, n - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * D8 + 16 * (kc ^ (kr & 7))),
+                                       (lds_void8*)(smem + stg * 2 * TILEB + i * 1024), 16, 0, 0);
+      const int d = 16 * i + (lane >> 2), vc = lane & 3;
+      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)d * npad + kv0 + 16 * (vc ^ ((d >> 1) & 3))),
+                                       (lds_void8*)(smem + stg * 2 * TILEB + TILEB + i * 1024), 16, 0, 0);
+    }
+  };
+
+  // this lane's query row as B operands: bytes 64 ks + 32 half .. +31
+  i32x8 qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q8) + (((int64_t)b * p.heads_q + hq) * n + row) * D8 + 64 * ks + 32 * half;
+    const u32x4 a = row < n ? *reinterpret_cast<const u32x4*>(qp) : u32x4{0, 0, 0, 0};
+    const u32x4 c = row < n ? *reinterpret_cast<const u32x4*>(qp + 16) : u32x4{0, 0, 0, 0};
+    qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  }
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // e4m3 1.0 in every byte
+
+  const float c2 = p.scale_log2 * qs;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 o[4], lsum = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+
+  for (int i = 0; i < ST8 - 1; ++i)
+    if (i < ntiles) issue(i, i);
+  for (int j = 0; j < ntiles; ++j) {
+    const int stg = j % ST8;
+    if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt((4 & 15) | ((4 >> 4) << 14) | (7 << 4) | (15 << 8));   // tile j landed, j+1 may fly
+    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();                         // for every wave; tile j-1's stage is free
+    if (j + ST8 - 1 < ntiles) issue(j + ST8 - 1, (j + ST8 - 1) % ST8);
+    if (j >= nt_w) continue;                 // wholly in this wave's future
+
+    const uint8_t* ks_ = smem + stg * 2 * TILEB;
+    const uint8_t* vs_ = ks_ + TILEB;
+    const int kv0 = j * KT;
+    f32x16 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x16{};
+      const int kr = 32 * blk + r32;         // key row of this lane's A fragment
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 4 * ks + 2 * half;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * (c0 ^ (kr & 7)));
+        const u32x4 c = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * ((c0 + 1) ^ (kr & 7)));
+        const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+        sc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], sc[blk], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    // softmax: register j of block blk holds key kv0 + 32 blk + 8(j/4) + 4 half + j%4
+    const float ce = c2 * ksc[j];
+    const bool edge = (CAUSAL && kv0 + KT - 1 > wrow0) || (kv0 + KT > n);
+    float mx = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int key = kv0 + 32 * blk + 8 * (jj >> 2) + 4 * half + (jj & 3);
+        float x = sc[blk][jj] * ce;
+        if (edge && ((CAUSAL && key > row) || key >= n)) x = kNegInf;
+        sc[blk][jj] = x;
+        mx = fmaxf(mx, x);
+      }
+    const float mt = half_swap_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mt > m_run)) {      // integer base: every rescale is a power of two
+      const float m_new = mt > m_run ? ceilf(mt) : m_run;
+      const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float mu = m_run == kNegInf ? 0.f : m_run;
+    i32x8 pf;
+    float rs = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bidx = 4 * w + e;                      // byte b: block b/16, register b%16
+        pr[e] = fast_exp2(sc[bidx >> 4][bidx & 15] - mu);
+        rs += pr[e];
+      }
+      int word = pack2<false>(fminf(pr[0] * 256.f, 448.f), fminf(pr[1] * 256.f, 448.f), 0);
+      pf[w] = pack2<true>(fminf(pr[2] * 256.f, 448.f), fminf(pr[3] * 256.f, 448.f), word);
+    }
+    l_run += half_swap_sum(rs);
+    // O^T += V^T P^T: lane (d = 32 db + lane % 32, half) reads positions 32 half .. +31 of row d
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + r32, sw = (d >> 1) & 3;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(vs_ + d * KT + 16 * ((2 * half) ^ sw));
+      const u32x4 c = *reinterpret_cast<const u32x4*>(vs_ + d * KT + 16 * ((2 * half + 1) ^ sw));
+      const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[db], 0, 0, 0, 127, 0, 127);
+    }
+    lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lsum, 0, 0, 0, 127, 0, 127);
+  }
+
+  if (row < n) {
+    const float inv_l = lsum[0] > 0.f ? vs / lsum[0] : 0.f;
+    TOut* op = reinterpret_cast<TOut*>(p.o) + (((int64_t)b * p.heads_q + hq) * n + row) * D8;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * half;
+        const float v0 = o[db][4 * gq] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
+        const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
+        if constexpr (sizeof(TOut) == 4) {
+          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+        } else {
+          bf16x4 hh;
+          hh[0] = (__bf16)v0; hh[1] = (__bf16)v1; hh[2] = (__bf16)v2; hh[3] = (__bf16)v3;
+          *reinterpret_cast<bf16x4*>(op + d) = hh;
+        }
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[((int64_t)b * p.heads_q + hq) * n + row] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace detail
+
+hipError_t launch_fp8_quant(const Fp8QuantParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((detail::fp8_quant_qk_kernel<QB>),
+                     dim3((unsigned)((p.seqlen + QB - 1) / QB), (unsigned)p.heads_q, (unsigned)p.batch), dim3(256), 0,
+                     stream, p, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((detail::fp8_quant_qk_kernel<KT>),
+                     dim3((unsigned)((p.seqlen + KT - 1) / KT), (unsigned)p.heads_kv, (unsigned)p.batch), dim3(256), 0,
+                     stream, p, 1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(detail::fp8_quant_v_kernel, dim3((unsigned)p.heads_kv, (unsigned)p.batch), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
+  const int64_t wgs = (int64_t)p.batch * p.heads_q * ((p.seqlen + 127) / 128);
+  if (p.causal) {
+    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, float>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, __bf16>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+  } else {
+    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, float>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, __bf16>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

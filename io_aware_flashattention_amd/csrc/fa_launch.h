@@ -64,6 +64,44 @@ struct BwdParams {
   bool causal, grad_fp32, o_fp32;
 };
 
+// FP8 path (head_dim 128): the quantiser's inputs and outputs, then the
+// attention kernel's. Quantised tensors are contiguous:
+//   q8 [B, Hq, N, 128] e4m3 (rotated), q_scale [B, Hq, ceil(N/128)]
+//   k8 [B, Hkv, N, 128] e4m3 (rotated), k_scale [B, Hkv, ceil(N/64)]
+//   v8t [B, Hkv, 128, Npad] e4m3, Npad = 64 ceil(N/64), keys permuted in
+//   every 64-key tile; v_scale [B, Hkv]
+struct Fp8QuantParams {
+  const void* q;       // bf16 [B, Hq, N, 128], strides q_stride
+  const void* k;       // bf16 [B, Hkv, N, 128], strides kv_stride (shared by v)
+  const void* v;
+  const float* signs;  // [128] +-1, or null (no rotation)
+  void* q8;
+  void* k8;
+  void* v8t;
+  float* q_scale;
+  float* k_scale;
+  float* v_scale;
+  int64_t q_stride[3], kv_stride[3];
+  int batch, heads_q, heads_kv, seqlen;
+};
+
+struct Fp8FwdParams {
+  const void* q8;
+  const void* k8;
+  const void* v8t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;             // [B, Hq, N, 128] contiguous, bf16 or float32
+  float* lse;          // [B, Hq, N] or null
+  int batch, heads_q, heads_kv, group, seqlen;
+  float scale_log2;
+  bool causal, out_fp32;
+};
+
+hipError_t launch_fp8_quant(const Fp8QuantParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+
 // n_qtiles is filled in by the launchers (it depends on the kernel's row tile).
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);       // dispatches on in_fp32
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);

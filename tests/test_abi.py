@@ -159,6 +159,51 @@ def test_bwd_workspace_size():
     assert lib.fa_bwd_workspace_bytes(0, 8, 100) == 0
 
 
+def _fp8q(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, s=None, B=1, Hq=4, Hkv=2, N=64, d=128,
+             qs=(4 * 64 * 128, 64 * 128, 128), ks=(2 * 64 * 128, 64 * 128, 128), q8=FAKE + 0x300000,
+             k8=FAKE + 0x400000, v8=FAKE + 0x500000, sq=FAKE + 0x600000, sk=FAKE + 0x700000, sv=FAKE + 0x800000)
+    a.update(kw)
+    arr = lambda t: (ctypes.c_int64 * 3)(*t) if t is not None else None
+    st = lib.fa_fp8_quantize(a["q"], a["k"], a["v"], a["s"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], arr(a["qs"]),
+                             arr(a["ks"]), a["q8"], a["k8"], a["v8"], a["sq"], a["sk"], a["sv"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+def _fp8f(**kw):
+    lib = _lib.load()
+    a = dict(q8=FAKE, k8=FAKE + 0x100000, v8=FAKE + 0x200000, sq=FAKE + 0x300000, sk=FAKE + 0x400000,
+             sv=FAKE + 0x500000, o=FAKE + 0x600000, lse=None, B=1, Hq=4, Hkv=2, N=64, d=128, outd=0, mask=1,
+             scale=0.088)
+    a.update(kw)
+    st = lib.fa_fwd_fp8(a["q8"], a["k8"], a["v8"], a["sq"], a["sk"], a["sv"], a["o"], a["lse"], a["B"], a["Hq"],
+                        a["Hkv"], a["N"], a["d"], a["outd"], a["mask"], a["scale"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn,kw,status,needle", [
+    (_fp8q, dict(v8=None), 1, "non-null"),
+    (_fp8q, dict(qs=None), 1, "stride"),
+    (_fp8q, dict(N=0), 1, "positive"),
+    (_fp8q, dict(d=64), 2, "head_dim"),
+    (_fp8q, dict(Hq=3, Hkv=2), 2, "multiple"),
+    (_fp8q, dict(k8=FAKE + 0x400008), 2, "aligned"),
+    (_fp8q, dict(ks=(2 * 64 * 128, 64 * 128, 132)), 2, "multiples"),
+    (_fp8f, dict(sv=None), 1, "non-null"),
+    (_fp8f, dict(Hkv=0), 1, "positive"),
+    (_fp8f, dict(scale=0.0), 1, "softmax_scale"),
+    (_fp8f, dict(outd=4), 1, "out_dtype"),
+    (_fp8f, dict(mask=9), 1, "mask"),
+    (_fp8f, dict(d=256), 2, "head_dim"),
+    (_fp8f, dict(o=FAKE + 0x600004), 2, "aligned"),
+])
+def test_fp8_rejects_before_launch(fn, kw, status, needle):
+    st, msg = fn(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def _dec(**kw):
     lib = _lib.load()
     a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lens=FAKE + 0x300000, o=FAKE + 0x400000, lse=None,

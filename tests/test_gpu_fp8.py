@@ -1,0 +1,110 @@
+"""GPU parity of the FP8 path (fa_fp8_quantize, fa_fwd_fp8) against oracle/fp8.py.
+
+The quantiser decides its codes in float32 exactly as the oracle does (same
+butterfly order, same scale formula, nearest-even e4m3), so codes and scales
+must match bit for bit. The attention kernel quantises its probabilities from
+float32 exponentials: a weight whose value lies within an ulp or two of an
+e4m3 rounding boundary can round the other way than in the fp64 oracle, which
+moves O by at most one e4m3 step of that weight (2^-4 of it). The gate is
+therefore O mean-abs <= 1e-3 and max-abs <= 0.1 (one step of a dominant
+weight times |V| <= 1.6) on the float32 output. The LSE gate is 2e-3: the
+fp8 matrix core does not accumulate its 64-product dot products exactly in
+float32 (scores of about 35 in base 2 on the x8-key rows came out with up to
+9.5e-4 of LSE error although every product of two e4m3 codes is exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_flashattention_amd import workloads as W
+from oracle import attention_ref, fp8_attention_ref, quantize
+from tests.parity import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+O_MEAN, O_MAX, LSE_MAX = 1e-3, 0.1, 2e-3
+
+
+def fa():
+    import io_aware_flashattention_amd as m
+    return m
+
+
+def vpos(kappa: int) -> int:
+    """Position of key kappa inside a 64-key tile of the transposed V storage (header formula)."""
+    return 32 * ((kappa // 4) % 2) + 16 * (kappa // 32) + 4 * ((kappa % 32) // 8) + kappa % 4
+
+
+def signs_for(seed: int) -> np.ndarray:
+    return np.random.default_rng([seed, 7]).choice([-1.0, 1.0], 128).astype(np.float32)
+
+
+def gpu_quant(q, k, v, signs):
+    s = torch.from_numpy(signs).to("cuda") if signs is not None else None
+    out = fa().fp8_quantize(to_dev(q), to_dev(k), to_dev(v), s)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 70, 129, 300])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_quantiser_codes_and_scales_match(N, rotate):
+    say(f"case fp8 quantiser N={N} rotate={rotate}")
+    q, k, v = W.make_random_prefill(1, 4, 2, N, N, 128, seed=1100 + N, heavy_frac=0.01)
+    signs = signs_for(N)
+    got = gpu_quant(q, k, v, signs if rotate else None)
+    ref = quantize(W.to_f64(q), W.to_f64(k), W.to_f64(v), signs, rotate=rotate)
+    assert np.array_equal(got["q8"].float().cpu().numpy(), ref["q8"])
+    assert np.array_equal(got["k8"].float().cpu().numpy(), ref["k8"])
+    assert np.array_equal(got["q_scale"].cpu().numpy(), ref["sq"])
+    assert np.array_equal(got["k_scale"].cpu().numpy(), ref["sk"])
+    assert np.array_equal(got["v_scale"].cpu().numpy(), ref["sv"][..., 0])
+    v8t = got["v8t"].float().cpu().numpy()                      # [B, Hkv, 128, npad]
+    npad = v8t.shape[-1]
+    perm = np.array([t * 64 + vpos(kk) for t in range(npad // 64) for kk in range(64)])
+    v8 = v8t[..., perm].transpose(0, 1, 3, 2)                   # back to [B, Hkv, npad, 128]
+    assert np.array_equal(v8[:, :, :N], ref["v8"]) and np.all(v8[:, :, N:] == 0)
+
+
+def _check(o, lse, o_ref, l_ref, what):
+    o = o.detach().float().cpu().numpy().astype(np.float64)
+    ln = lse.detach().cpu().numpy().astype(np.float64)
+    e, el = np.abs(o - o_ref), np.abs(ln - l_ref)
+    say(f"  {what}: O max {e.max():.3e} mean {e.mean():.3e}  LSE max {el.max():.3e}")
+    assert np.all(np.isfinite(o))
+    assert e.mean() <= O_MEAN and e.max() <= O_MAX and el.max() <= LSE_MAX, what
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 70, 129, 300, 1000])
+def test_fp8_attention_matches_oracle(N, causal):
+    say(f"case fp8 attention N={N} causal={causal}")
+    q, k, v = W.make_random_prefill(1, 8, 2, N, N, 128, seed=1200 + N, heavy_frac=0.01)
+    signs = signs_for(N)
+    got = gpu_quant(q, k, v, signs)
+    o, lse = fa().fwd_fp8(got, causal=causal, out_dtype=torch.float32)
+    o16, _ = fa().fwd_fp8(got, causal=causal, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o.to(torch.bfloat16))
+    quant = quantize(W.to_f64(q), W.to_f64(k), W.to_f64(v), signs)
+    o_ref, l_ref = fp8_attention_ref(quant, 1 / np.sqrt(128), causal=causal)
+    _check(o, lse, o_ref, l_ref, f"fp8 N={N} causal={causal}")
+    o_ex, _ = attention_ref(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / np.sqrt(128), causal=causal)
+    say(f"  (against exact attention: O mean {np.abs(o.cpu().numpy() - o_ex).mean():.3e})")
+
+
+def test_fp8_long_context_gqa_sampled():
+    """The long-context GQA workload (64 query / 8 kv heads, 8192 tokens, 1% of
+    K rows x8), causal, on sampled rows of every head."""
+    cfg = W.CONFIGS["c4a_gqa_8k"]
+    say(f"case fp8 {cfg.name} sampled rows")
+    q, k, v = W.make_prefill_inputs(cfg)
+    signs = signs_for(cfg.seed)
+    got = gpu_quant(q, k, v, signs)
+    o, lse = fa().fwd_fp8(got, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
+    quant = quantize(W.to_f64(q), W.to_f64(k), W.to_f64(v), signs)
+    o_ref, l_ref = fp8_attention_ref(quant, cfg.scale, causal=True, rows=rows)
+    _check(o[:, :, rows], lse[:, :, rows], o_ref[:, :, rows], l_ref[:, :, rows], f"fp8 {cfg.name}")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
