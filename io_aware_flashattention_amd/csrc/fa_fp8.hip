@@ -34,6 +34,13 @@ constexpr int QB = 128;      // query rows per scale block (and per attention wo
 constexpr int KT = 64;       // keys per scale block and per tile
 constexpr int ST8 = 3;       // K/V tile ring depth
 
+#ifndef FA_FP8_WPE
+#define FA_FP8_WPE 2         // waves per SIMD the attention kernel is register-limited to
+#endif
+#ifndef FA_FP8_RAWBAR
+#define FA_FP8_RAWBAR 1      // barrier without the vmcnt(0) fence of __syncthreads
+#endif
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void8;
 // per-tile scales are read at wave-uniform addresses through the constant
@@ -200,7 +207,8 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p
 
 // Attention on the quantised operands: 4 waves x 32 query rows per workgroup.
 template <bool CAUSAL, typename TOut>
-__global__ __launch_bounds__(256) void fwd_fp8_kernel(const Fp8FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FP8_WPE, FA_FP8_WPE)))
+void fwd_fp8_kernel(const Fp8FwdParams p) {
   constexpr int NW = 4, BRW = 32 * NW, TILEB = KT * D8;   // bytes per K (or V^T) tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST8 * 2 * TILEB];  // [stage][K, V^T][8 KB]
 
@@ -267,7 +275,15 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const Fp8FwdParams p) {
     const int stg = j % ST8;
     if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt((4 & 15) | ((4 >> 4) << 14) | (7 << 4) | (15 << 8));   // tile j landed, j+1 may fly
     else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+#if FA_FP8_RAWBAR
+    // every wave has waited for its own loads of tile j; the barrier publishes
+    // them and frees tile j-1's stage, while tile j+1's loads stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#else
     __syncthreads();                         // for every wave; tile j-1's stage is free
+#endif
     if (j + ST8 - 1 < ntiles) issue(j + ST8 - 1, (j + ST8 - 1) % ST8);
     if (j >= nt_w) continue;                 // wholly in this wave's future
 
