@@ -263,8 +263,11 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
 // dQ for 128 query rows of one (batch, query head), walking the keys 64 at a
 // time (two 32-key blocks) with the next 64 prefetched. Under the causal
 // mask the heaviest query tiles are dispatched first.
+// (Capped at two waves per SIMD: 256 registers hold it without spills, and
+// the second wave's matrix work overlaps this one's softmax.)
 template <int D, bool CAUSAL, typename TOut>
-__global__ __launch_bounds__(NWB * 64) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(NWB * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, KB2 = 2 * BB;
   __shared__ __attribute__((aligned(16))) __bf16 ks[KB2 * D];
   __shared__ __attribute__((aligned(16))) __bf16 vs[KB2 * D];

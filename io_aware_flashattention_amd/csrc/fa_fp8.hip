@@ -37,6 +37,9 @@ constexpr int ST8 = 3;       // K/V tile ring depth
 #ifndef FA_FP8_WPE
 #define FA_FP8_WPE 2         // waves per SIMD the attention kernel is register-limited to
 #endif
+#ifndef FA_FP8_NW
+#define FA_FP8_NW 4          // waves (32 query rows each) per attention workgroup
+#endif
 #ifndef FA_FP8_RAWBAR
 #define FA_FP8_RAWBAR 1      // barrier without the vmcnt(0) fence of __syncthreads
 #endif
@@ -205,11 +208,13 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p
   }
 }
 
-// Attention on the quantised operands: 4 waves x 32 query rows per workgroup.
+// Attention on the quantised operands: FA_FP8_NW waves x 32 query rows per workgroup.
 template <bool CAUSAL, typename TOut>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FP8_WPE, FA_FP8_WPE)))
+__global__ __launch_bounds__(64 * FA_FP8_NW) __attribute__((amdgpu_waves_per_eu(FA_FP8_WPE, FA_FP8_WPE)))
 void fwd_fp8_kernel(const Fp8FwdParams p) {
-  constexpr int NW = 4, BRW = 32 * NW, TILEB = KT * D8;   // bytes per K (or V^T) tile
+  constexpr int NW = FA_FP8_NW, BRW = 32 * NW, TILEB = KT * D8;   // bytes per K (or V^T) tile
+  constexpr int LPW = 8 / NW;                // 1-KB DMA writes per wave per operand tile
+  static_assert(8 % NW == 0, "");
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST8 * 2 * TILEB];  // [stage][K, V^T][8 KB]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
@@ -228,18 +233,18 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k8) + ((int64_t)b * p.heads_kv + kvh) * n * D8;
   const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v8t) + ((int64_t)b * p.heads_kv + kvh) * D8 * npad;
   const const_f32* ksc = (const const_f32*)p.k_scale + ((int64_t)b * p.heads_kv + kvh) * (npad / KT);
-  const float qs = p.q_scale[((int64_t)b * p.heads_q + hq) * ((n + QB - 1) / QB) + q0 / QB];
+  const float qs = p.q_scale[((int64_t)b * p.heads_q + hq) * ((n + QB - 1) / QB) + wrow0 / QB];
   const float vs = p.v_scale[(int64_t)b * p.heads_kv + kvh];
 
-  // DMA: a tile is 8 K writes and 8 V^T writes of 1 KB; wave w issues two of each.
+  // DMA: a tile is 8 K writes and 8 V^T writes of 1 KB; wave w issues LPW of each.
   // K: write i covers rows 8i..8i+7 (16-byte chunk lane%8 of row 8i + lane/8);
   // V^T: write i covers d rows 16i..16i+15 (chunk lane%4 of row 16i + lane/4).
   // The global chunk is XOR-swizzled by the row, so reads below XOR back.
   auto issue = [&](int tile, int stg) {
     const int kv0 = tile * KT;
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-      const int i = 2 * wave + i2;
+    for (int i2 = 0; i2 < LPW; ++i2) {
+      const int i = LPW * wave + i2;
       const int kr = 8 * i + (lane >> 3), kc = lane & 7;
       const int key = min(kv0 + kr, n - 1);
       __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * D8 + 16 * (kc ^ (kr & 7))),
@@ -273,7 +278,7 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     if (i < ntiles) issue(i, i);
   for (int j = 0; j < ntiles; ++j) {
     const int stg = j % ST8;
-    if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt((4 & 15) | ((4 >> 4) << 14) | (7 << 4) | (15 << 8));   // tile j landed, j+1 may fly
+    if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt((2 * LPW) | (7 << 4) | (15 << 8));   // tile j landed, j+1 may fly
     else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 #if FA_FP8_RAWBAR
     // every wave has waited for its own loads of tile j; the barrier publishes
@@ -397,13 +402,13 @@ hipError_t launch_fp8_quant(const Fp8QuantParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
-  const int64_t wgs = (int64_t)p.batch * p.heads_q * ((p.seqlen + 127) / 128);
+  const int64_t wgs = (int64_t)p.batch * p.heads_q * ((p.seqlen + 32 * FA_FP8_NW - 1) / (32 * FA_FP8_NW));
   if (p.causal) {
-    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, float>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, __bf16>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, float>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
+    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, __bf16>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
   } else {
-    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, float>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, __bf16>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, float>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
+    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, __bf16>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
   }
   return hipGetLastError();
 }
