@@ -18,7 +18,7 @@
 // 32-key blocks of two k-steps, the softmax in float32 with the tile's
 // q-scale x k-scale folded into the one FMA per score, and O^T += V^T P^T
 // with P quantised to e4m3 as 2^8 * 2^(x - m) against an integer base m that
-// moves with the row maximum (so every rescale is an exact power of two and
+// moves with the row maximum (one FMA and one exponential per score) (so every rescale is an exact power of two and
 // every weight keeps three mantissa bits down to 2^-14 of the largest). O is
 // divided by the sum of the quantised weights (one more MFMA against a row of
 // ones) and multiplied by V's scale; the LSE uses the float32 sum.
@@ -309,21 +309,24 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
         sc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], sc[blk], 0, 0, 0, 127, 0, 127);
       }
     }
-    // softmax: register j of block blk holds key kv0 + 32 blk + 8(j/4) + 4 half + j%4
+    // softmax: register j of block blk holds key kv0 + 32 blk + 8(j/4) + 4 half + j%4.
+    // The maximum is taken on the raw scores (the tile's scale ce is positive),
+    // and one FMA per score both scales and subtracts the base; the base is
+    // lowered by 8 so the weights come out as 2^8 * 2^(x - m), ready for e4m3.
     const float ce = c2 * ksc[j];
     const bool edge = (CAUSAL && kv0 + KT - 1 > wrow0) || (kv0 + KT > n);
-    float mx = kNegInf;
+    float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        const int key = kv0 + 32 * blk + 8 * (jj >> 2) + 4 * half + (jj & 3);
-        float x = sc[blk][jj] * ce;
-        if (edge && ((CAUSAL && key > row) || key >= n)) x = kNegInf;
-        sc[blk][jj] = x;
-        mx = fmaxf(mx, x);
+        if (edge) {
+          const int key = kv0 + 32 * blk + 8 * (jj >> 2) + 4 * half + (jj & 3);
+          if ((CAUSAL && key > row) || key >= n) sc[blk][jj] = kNegInf;
+        }
+        mq[(2 * blk + (jj >> 3)) & 3] = fmaxf(mq[(2 * blk + (jj >> 3)) & 3], sc[blk][jj]);
       }
-    const float mt = half_swap_max(mx);
+    const float mt = half_swap_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * ce;
     if (__builtin_amdgcn_ballot_w64(mt > m_run)) {      // integer base: every rescale is a power of two
       const float m_new = mt > m_run ? ceilf(mt) : m_run;
       const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
@@ -333,22 +336,22 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
       m_run = m_new;
     }
-    const float mu = m_run == kNegInf ? 0.f : m_run;
+    const float mb = (m_run == kNegInf ? 0.f : m_run) - 8.f;
     i32x8 pf;
-    float rs = 0.f;
+    float rq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float pr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int bidx = 4 * w + e;                      // byte b: block b/16, register b%16
-        pr[e] = fast_exp2(sc[bidx >> 4][bidx & 15] - mu);
-        rs += pr[e];
+        pr[e] = fast_exp2(fmaf(sc[bidx >> 4][bidx & 15], ce, -mb));   // <= 2^8
+        rq[e] += pr[e];
       }
-      int word = pack2<false>(fminf(pr[0] * 256.f, 448.f), fminf(pr[1] * 256.f, 448.f), 0);
-      pf[w] = pack2<true>(fminf(pr[2] * 256.f, 448.f), fminf(pr[3] * 256.f, 448.f), word);
+      const int word = pack2<false>(pr[0], pr[1], 0);
+      pf[w] = pack2<true>(pr[2], pr[3], word);
     }
-    l_run += half_swap_sum(rs);
+    l_run += half_swap_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));   // in units of 2^-8
     // O^T += V^T P^T: lane (d = 32 db + lane % 32, half) reads positions 32 half .. +31 of row d
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -380,7 +383,7 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
         }
       }
     if (p.lse != nullptr && half == 0)
-      p.lse[((int64_t)b * p.heads_q + hq) * n + row] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+      p.lse[((int64_t)b * p.heads_q + hq) * n + row] = l_run > 0.f ? (m_run + __log2f(l_run) - 8.f) * kLn2 : kNegInf;
   }
 }
 
