@@ -32,16 +32,13 @@ namespace {
 constexpr int D8 = 128;      // head dim
 constexpr int QB = 128;      // query rows per scale block (and per attention workgroup)
 constexpr int KT = 64;       // keys per scale block and per tile
-constexpr int ST8 = 3;       // K/V tile ring depth
+constexpr int ST8 = 4;       // K/V tile ring depth (two tiles in flight beyond the two in use)
 
 #ifndef FA_FP8_WPE
 #define FA_FP8_WPE 2         // waves per SIMD the attention kernel is register-limited to
 #endif
 #ifndef FA_FP8_NW
 #define FA_FP8_NW 4          // waves (32 query rows each) per attention workgroup
-#endif
-#ifndef FA_FP8_RAWBAR
-#define FA_FP8_RAWBAR 1      // barrier without the vmcnt(0) fence of __syncthreads
 #endif
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +52,7 @@ template <bool HI>
 __device__ __forceinline__ int pack2(float a, float b, int w) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, HI);
 }
+template <bool B> struct bool_c { static constexpr bool value = B; };
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
 
 // position of key kappa (0..63) of a tile in the transposed V storage: the
@@ -209,7 +207,7 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p
 }
 
 // Attention on the quantised operands: FA_FP8_NW waves x 32 query rows per workgroup.
-template <bool CAUSAL, typename TOut>
+template <typename TOut>
 __global__ __launch_bounds__(64 * FA_FP8_NW) __attribute__((amdgpu_waves_per_eu(FA_FP8_WPE, FA_FP8_WPE)))
 void fwd_fp8_kernel(const Fp8FwdParams p) {
   constexpr int NW = FA_FP8_NW, BRW = 32 * NW, TILEB = KT * D8;   // bytes per K (or V^T) tile
@@ -218,17 +216,19 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST8 * 2 * TILEB];  // [stage][K, V^T][8 KB]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
+  // one instance serves both masks: the flag is uniform, and the loop keeps one register allocation
+  const bool causal = p.causal;
   const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
   const int nqt = (n + BRW - 1) / BRW;
   const int t = blockIdx.x % nqt;
   const int bh = blockIdx.x / nqt;
   const int hq = bh % p.heads_q, b = bh / p.heads_q;
   const int kvh = hq / p.group;
-  const int qt = CAUSAL ? nqt - 1 - t : t;   // heavy tiles first
+  const int qt = causal ? nqt - 1 - t : t;   // heavy tiles first
   const int q0 = qt * BRW, wrow0 = q0 + wave * 32, row = wrow0 + r32;
-  const int kv_end = CAUSAL ? min(n, q0 + BRW) : n;
+  const int kv_end = causal ? min(n, q0 + BRW) : n;
   const int ntiles = (kv_end + KT - 1) / KT;
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / KT + 1) : ntiles;
+  const int nt_w = causal ? min(ntiles, (wrow0 + 31) / KT + 1) : ntiles;
 
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k8) + ((int64_t)b * p.heads_kv + kvh) * n * D8;
   const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v8t) + ((int64_t)b * p.heads_kv + kvh) * D8 * npad;
@@ -264,41 +264,24 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     const u32x4 c = row < n ? *reinterpret_cast<const u32x4*>(qp + 16) : u32x4{0, 0, 0, 0};
     qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
-  i32x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // e4m3 1.0 in every byte
+  // 1.0 in every e2m1 (fp4) nibble: as the fp4 A operand of the weight-sum
+  // product it covers a lane's 32 k values in four registers
+  const i32x8 ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
 
   const float c2 = p.scale_log2 * qs;
   float m_run = kNegInf, l_run = 0.f;
-  f32x16 o[4], lsum = f32x16{};
+  i32x8 pf = {};                             // this tile's e4m3 weights (B operand of O^T += V^T P^T)
+  f32x16 o[4], ls = f32x16{};                // ls: the last tile's sum of e4m3 weights, every register
+  float l8 = 0.f;                            // sum of e4m3 weights of the earlier tiles
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  for (int i = 0; i < ST8 - 1; ++i)
-    if (i < ntiles) issue(i, i);
-  for (int j = 0; j < ntiles; ++j) {
-    const int stg = j % ST8;
-    if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt((2 * LPW) | (7 << 4) | (15 << 8));   // tile j landed, j+1 may fly
-    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-#if FA_FP8_RAWBAR
-    // every wave has waited for its own loads of tile j; the barrier publishes
-    // them and frees tile j-1's stage, while tile j+1's loads stay in flight
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-#else
-    __syncthreads();                         // for every wave; tile j-1's stage is free
-#endif
-    if (j + ST8 - 1 < ntiles) issue(j + ST8 - 1, (j + ST8 - 1) % ST8);
-    if (j >= nt_w) continue;                 // wholly in this wave's future
-
-    const uint8_t* ks_ = smem + stg * 2 * TILEB;
-    const uint8_t* vs_ = ks_ + TILEB;
-    const int kv0 = j * KT;
-    f32x16 sc[2];
+  // S^T tile = K Q^T for the 64 keys of a tile: block blk holds keys 32 blk .. +31
+  auto scores = [&](int tile, f32x16 (&s)[2]) {
+    const uint8_t* ks_ = smem + (tile % ST8) * 2 * TILEB;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = f32x16{};
+      s[blk] = f32x16{};
       const int kr = 32 * blk + r32;         // key row of this lane's A fragment
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -306,50 +289,66 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * (c0 ^ (kr & 7)));
         const u32x4 c = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * ((c0 + 1) ^ (kr & 7)));
         const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-        sc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], sc[blk], 0, 0, 0, 127, 0, 127);
+        s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], s[blk], 0, 0, 0, 127, 0, 127);
       }
     }
-    // softmax: register j of block blk holds key kv0 + 32 blk + 8(j/4) + 4 half + j%4.
+  };
+  // every wave has waited for its own loads of tiles j and j+1; the barrier
+  // publishes them and frees the stage of tile j-1 (its K was read two steps
+  // ago, its V one step ago), which takes tile j+ST8-1
+  auto sync_tile = [&](int j) {
+    if (j + 2 < ntiles) __builtin_amdgcn_s_waitcnt((2 * LPW) | (7 << 4) | (15 << 8));   // tile j+2 may fly
+    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + ST8 - 1 < ntiles) issue(j + ST8 - 1, (j + ST8 - 1) % ST8);
+  };
+  auto softmax_pv = [&](auto edge_c, int j, f32x16 (&sc)[2]) {
+    constexpr bool EDGE = decltype(edge_c)::value;   // the tile holds masked keys
+    const uint8_t* vs_ = smem + (j % ST8) * 2 * TILEB + TILEB;
+    const int kv0 = j * KT;
+    // softmax: register jj of block blk holds key kv0 + 32 blk + 8(jj/4) + 4 half + jj%4.
     // The maximum is taken on the raw scores (the tile's scale ce is positive),
     // and one FMA per score both scales and subtracts the base; the base is
     // lowered by 8 so the weights come out as 2^8 * 2^(x - m), ready for e4m3.
+    l8 += ls[0];                             // the previous tile's weights, at the current base
     const float ce = c2 * ksc[j];
-    const bool edge = (CAUSAL && kv0 + KT - 1 > wrow0) || (kv0 + KT > n);
+    // a key is visible when key <= lim; relative to this lane's first key of the tile
+    const int rel = (causal ? min(row, n - 1) : n - 1) - kv0 - 4 * half;
+    float x[2][16];
     float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        if (edge) {
-          const int key = kv0 + 32 * blk + 8 * (jj >> 2) + 4 * half + (jj & 3);
-          if ((CAUSAL && key > row) || key >= n) sc[blk][jj] = kNegInf;
-        }
-        mq[(2 * blk + (jj >> 3)) & 3] = fmaxf(mq[(2 * blk + (jj >> 3)) & 3], sc[blk][jj]);
+        x[blk][jj] = sc[blk][jj];
+        if (EDGE) x[blk][jj] = 32 * blk + 8 * (jj >> 2) + (jj & 3) > rel ? kNegInf : x[blk][jj];
+        mq[(2 * blk + (jj >> 3)) & 3] = fmaxf(mq[(2 * blk + (jj >> 3)) & 3], x[blk][jj]);
       }
     const float mt = half_swap_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * ce;
     if (__builtin_amdgcn_ballot_w64(mt > m_run)) {      // integer base: every rescale is a power of two
       const float m_new = mt > m_run ? ceilf(mt) : m_run;
       const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
-      lsum *= alpha;
+      l8 *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
       m_run = m_new;
     }
     const float mb = (m_run == kNegInf ? 0.f : m_run) - 8.f;
-    i32x8 pf;
-    float rq[4] = {0.f, 0.f, 0.f, 0.f};
+    float rq[4];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float pr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int bidx = 4 * w + e;                      // byte b: block b/16, register b%16
-        pr[e] = fast_exp2(fmaf(sc[bidx >> 4][bidx & 15], ce, -mb));   // <= 2^8
-        rq[e] += pr[e];
+        pr[e] = fast_exp2(fmaf(x[bidx >> 4][bidx & 15], ce, -mb));    // <= 2^8
+        rq[e] = w == 0 ? pr[e] : rq[e] + pr[e];
       }
-      const int word = pack2<false>(pr[0], pr[1], 0);
-      pf[w] = pack2<true>(pr[2], pr[3], word);
+      // both halves of the word are rewritten: the previous tile's word is only a placeholder
+      pf[w] = pack2<true>(pr[2], pr[3], pack2<false>(pr[0], pr[1], pf[w]));
     }
     l_run += half_swap_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));   // in units of 2^-8
     // O^T += V^T P^T: lane (d = 32 db + lane % 32, half) reads positions 32 half .. +31 of row d
@@ -361,11 +360,35 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
       const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
       o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[db], 0, 0, 0, 127, 0, 127);
     }
-    lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lsum, 0, 0, 0, 127, 0, 127);
+    ls = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, f32x16{}, 4, 0, 0, 127, 0, 127);   // A: fp4
+  };
+
+  // Software pipeline: step j issues the score MFMAs of tile j+1, which run on
+  // the matrix cores while the vector unit takes tile j's softmax.
+  for (int i = 0; i < ST8 - 1; ++i)
+    if (i < ntiles) issue(i, i);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(0, sa);                             // every wave has at least one tile
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    sync_tile(j);
+    if (j + 1 < nt_w) scores(j + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < nt_w) {                          // later tiles are wholly in this wave's future
+      const int kv0 = j * KT;
+      if ((causal && kv0 + KT - 1 > wrow0) || kv0 + KT > n) softmax_pv(bool_c<true>{}, j, cur);
+      else softmax_pv(bool_c<false>{}, j, cur);
+    }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < ntiles) step(j + 1, sb, sa);
   }
+  l8 += ls[0];
 
   if (row < n) {
-    const float inv_l = lsum[0] > 0.f ? vs / lsum[0] : 0.f;
+    const float inv_l = l8 > 0.f ? vs / l8 : 0.f;
     TOut* op = reinterpret_cast<TOut*>(p.o) + (((int64_t)b * p.heads_q + hq) * n + row) * D8;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -406,13 +429,8 @@ hipError_t launch_fp8_quant(const Fp8QuantParams& p, hipStream_t stream) {
 
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   const int64_t wgs = (int64_t)p.batch * p.heads_q * ((p.seqlen + 32 * FA_FP8_NW - 1) / (32 * FA_FP8_NW));
-  if (p.causal) {
-    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, float>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
-    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<true, __bf16>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
-  } else {
-    if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, float>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
-    else hipLaunchKernelGGL((detail::fwd_fp8_kernel<false, __bf16>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
-  }
+  if (p.out_fp32) hipLaunchKernelGGL((detail::fwd_fp8_kernel<float>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
+  else hipLaunchKernelGGL((detail::fwd_fp8_kernel<__bf16>), dim3((unsigned)wgs), dim3(64 * FA_FP8_NW), 0, stream, p);
   return hipGetLastError();
 }
 
