@@ -112,6 +112,52 @@ __device__ __forceinline__ void store_rows(TOut* dst, const f32x16 (&acc)[D / 32
     }
 }
 
+
+// S and dP of a 32-row block (rows of the LDS tiles qt and gt) against this
+// wave's 32 keys: register j holds row acc_key(j, half), key = lane % 32.
+template <int D>
+__device__ __forceinline__ void dkdv_sdp(const __bf16* qt, const __bf16* gt, const bf16x8 (&kf)[D / 16],
+                                         const bf16x8 (&vf)[D / 16], int lane, f32x16& sa, f32x16& dp) {
+  sa = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    sa = mfma32(frag_sigma<D>(qt, lane, kc), kf[kc], sa);
+    dp = mfma32(frag_sigma<D>(gt, lane, kc), vf[kc], dp);
+  }
+}
+
+// P = exp2(S scale log2 e - LSE log2 e) and dS = P (dP - D), as bf16 B
+// operands; lse2 and dsum point at the block's 32 rows. EDGE applies the
+// mask (key past the end, or in the row's future under the causal mask).
+template <bool EDGE, bool CAUSAL>
+__device__ __forceinline__ void dkdv_probs(const f32x16& sa, const f32x16& dp, const float* lse2, const float* dsum,
+                                           int rs0, int key, int nk, float c2, int half, bf16x8 (&pb)[2],
+                                           bf16x8 (&sd)[2]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int rr = acc_key(j, half);
+    float x = fmaf(sa[j], c2, -lse2[rr]);
+    if (EDGE) x = key < nk && (!CAUSAL || key <= rs0 + rr) ? x : kNegInf;
+    const float pr = fast_exp2(x);
+    pb[j >> 3][j & 7] = (__bf16)pr;
+    sd[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dsum[rr]));
+  }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS for a 32-row block (rows are the contraction).
+template <int D>
+__device__ __forceinline__ void dkdv_acc(const __bf16* qt, const __bf16* gt, int lane, const bf16x8 (&pb)[2],
+                                         const bf16x8 (&sd)[2], f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      dv[db] = mfma32(frag_trans<D>(gt, lane, db, c), pb[c], dv[db]);
+      dk[db] = mfma32(frag_trans<D>(qt, lane, db, c), sd[c], dk[db]);
+    }
+}
+
 }  // namespace
 
 namespace detail {
@@ -223,33 +269,16 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
       for (int sb = 0; sb < 2; ++sb) {
         const int rs0 = r0 + sb * BB;
         if (CAUSAL && kw0 > rs0 + BB - 1) continue;   // every key of this wave is in these rows' future
-        const __bf16* qt = qs + sb * BB * D;
-        const __bf16* gt = gs + sb * BB * D;
-        // S and dP for (rows, keys): register j holds row acc_key(j, half), key = lane % 32
-        f32x16 sa = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < KS; ++kc) {
-          sa = mfma32(frag_sigma<D>(qt, lane, kc), kf[kc], sa);
-          dp = mfma32(frag_sigma<D>(gt, lane, kc), vf[kc], dp);
-        }
-        bf16x8 pb[2], sbf[2];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rr = sb * BB + acc_key(j, half);
-          const int row = r0 + rr;
-          const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
-          const float pr = vis ? fast_exp2(fmaf(sa[j], c2, -ls[rr])) : 0.f;
-          pb[j >> 3][j & 7] = (__bf16)pr;
-          sbf[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - ds[rr]));
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS (rows are the contraction)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dv[db] = mfma32(frag_trans<D>(gt, lane, db, c), pb[c], dv[db]);
-            dk[db] = mfma32(frag_trans<D>(qt, lane, db, c), sbf[c], dk[db]);
-          }
+        f32x16 sa, dp;
+        bf16x8 pb[2], sd[2];
+        dkdv_sdp<D>(qs + sb * BB * D, gs + sb * BB * D, kf, vf, lane, sa, dp);
+        // a masked element exists only on diagonal blocks and ragged keys;
+        // rows past the end carry LSE = +inf, so their weights are 0 already
+        if ((CAUSAL && kw0 + BB - 1 > rs0) || kw0 + BB > nk)
+          dkdv_probs<true, CAUSAL>(sa, dp, ls + sb * BB, ds + sb * BB, rs0, key, nk, c2, half, pb, sd);
+        else
+          dkdv_probs<false, CAUSAL>(sa, dp, ls + sb * BB, ds + sb * BB, rs0, key, nk, c2, half, pb, sd);
+        dkdv_acc<D>(qs + sb * BB * D, gs + sb * BB * D, lane, pb, sd, dv, dk);
       }
     }
     if (key < nk) {
