@@ -158,6 +158,7 @@ __device__ __forceinline__ void dkdv_acc(const __bf16* qt, const __bf16* gt, int
     }
 }
 
+
 }  // namespace
 
 namespace detail {
@@ -361,12 +362,13 @@ void bwd_dq_kernel(const BwdParams p) {
         dp = mfma32(frag_sigma<D>(vt, lane, kc), gf[kc], dp);
       }
       bf16x8 sbf[2];
+      // key kb0 + acc_key(j, half) is visible when acc_key(j, 0) <= lim (a
+      // row past the end has LSE = +inf, so its weights are 0 already)
+      const int lim = (CAUSAL ? min(row, nk - 1) : nk - 1) - kb0 - 8 * half;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = kb0 + acc_key(j, half);
-        const bool vis = key < nk && row < nq && (!CAUSAL || key <= row);
-        const float pr = vis ? fast_exp2(fmaf(sa[j], c2, -lse2)) : 0.f;
-        sbf[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dsum));
+        const float x = acc_key(j, 0) <= lim ? fmaf(sa[j], c2, -lse2) : kNegInf;
+        sbf[j >> 3][j & 7] = (__bf16)(fast_exp2(x) * (dp[j] - dsum));
       }
       // dQ^T += K^T dS^T (keys are the contraction)
 #pragma unroll
