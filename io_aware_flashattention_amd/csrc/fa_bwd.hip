@@ -31,6 +31,9 @@ namespace {
 
 constexpr int BB = 32;       // rows (or keys) per matrix-core block and per wave
 constexpr int NWB = 4;       // waves per workgroup
+#ifndef FA_BWD_AHEAD
+#define FA_BWD_AHEAD 2       // LDS fragment reads issued this many matrix steps ahead (dK/dV)
+#endif
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -115,16 +118,32 @@ __device__ __forceinline__ void store_rows(TOut* dst, const f32x16 (&acc)[D / 32
 
 // S and dP of a 32-row block (rows of the LDS tiles qt and gt) against this
 // wave's 32 keys: register j holds row acc_key(j, half), key = lane % 32.
+// Each k-step's two fragments are read FA_BWD_AHEAD steps before the MFMAs
+// that consume them (a scheduling barrier per step keeps that order), so
+// the LDS latency hides behind matrix work even with one wave per SIMD.
 template <int D>
 __device__ __forceinline__ void dkdv_sdp(const __bf16* qt, const __bf16* gt, const bf16x8 (&kf)[D / 16],
                                          const bf16x8 (&vf)[D / 16], int lane, f32x16& sa, f32x16& dp) {
+  constexpr int KS = D / 16, AHEAD = FA_BWD_AHEAD;
+  bf16x8 fq[KS], fg[KS];
+  auto read = [&](int kc) {
+    if (kc < KS) {
+      fq[kc] = frag_sigma<D>(qt, lane, kc);
+      fg[kc] = frag_sigma<D>(gt, lane, kc);
+    }
+  };
+#pragma unroll
+  for (int x = 0; x < AHEAD; ++x) read(x);
   sa = f32x16{};
   dp = f32x16{};
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    sa = mfma32(frag_sigma<D>(qt, lane, kc), kf[kc], sa);
-    dp = mfma32(frag_sigma<D>(gt, lane, kc), vf[kc], dp);
+  for (int kc = 0; kc < KS; ++kc) {
+    __builtin_amdgcn_sched_barrier(0);
+    read(kc + AHEAD);
+    sa = mfma32(fq[kc], kf[kc], sa);
+    dp = mfma32(fg[kc], vf[kc], dp);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // P = exp2(S scale log2 e - LSE log2 e) and dS = P (dP - D), as bf16 B
@@ -145,20 +164,30 @@ __device__ __forceinline__ void dkdv_probs(const f32x16& sa, const f32x16& dp, c
   }
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS for a 32-row block (rows are the contraction).
+// dV^T += dO^T P and dK^T += Q^T dS for a 32-row block (rows are the
+// contraction), with the transposing reads FA_BWD_AHEAD steps ahead.
 template <int D>
 __device__ __forceinline__ void dkdv_acc(const __bf16* qt, const __bf16* gt, int lane, const bf16x8 (&pb)[2],
                                          const bf16x8 (&sd)[2], f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      dv[db] = mfma32(frag_trans<D>(gt, lane, db, c), pb[c], dv[db]);
-      dk[db] = mfma32(frag_trans<D>(qt, lane, db, c), sd[c], dk[db]);
+  constexpr int DB = D / 32, NS = 2 * DB, AHEAD = FA_BWD_AHEAD;   // step i: row chunk i / DB, d block i % DB
+  bf16x8 fg[NS], fq[NS];
+  auto read = [&](int i) {
+    if (i < NS) {
+      fg[i] = frag_trans<D>(gt, lane, i % DB, i / DB);
+      fq[i] = frag_trans<D>(qt, lane, i % DB, i / DB);
     }
+  };
+#pragma unroll
+  for (int x = 0; x < AHEAD; ++x) read(x);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    read(i + AHEAD);
+    dv[i % DB] = mfma32(fg[i], pb[i / DB], dv[i % DB]);
+    dk[i % DB] = mfma32(fq[i], sd[i / DB], dk[i % DB]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
-
-
 }  // namespace
 
 namespace detail {
