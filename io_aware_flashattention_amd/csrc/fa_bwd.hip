@@ -38,11 +38,21 @@ constexpr int NWB = 4;       // waves per workgroup
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // 16-byte chunk swizzle of a tile row (any XOR pattern is correct as long as
-// every access of row r uses this row's value). It depends on r % 32 only,
+// every access of row r uses this row's value). It depends on r % 16 only,
 // so a 32-row block at row offset 32 b of a taller tile is addressed as a
-// 32-row tile at t + 32 b D.
+// 32-row tile at t + 32 b D. These tiles are read both ways, and the pattern
+// keeps both conflict-free on gfx950's 64 banks x 4 bytes:
+//   row fragments (ds_read_b128, 16 lanes at a time: rows 0-15 or 16-31 of a
+//     block at one chunk) need the pattern to permute the chunk slots of
+//     those 16 rows (for D = 64, two rows per 256-byte bank line: of its 8
+//     even and 8 odd rows);
+//   transposing reads (ds_read_b64_tr_b16, 32 lanes: 4 consecutive rows x 4
+//     consecutive chunks) need bit 2 and 3 of the pattern to differ across
+//     the 4 rows (for D = 64, bit 2 across the two rows of each parity).
+// 4 (r % 4) + (r / 4) % 4 meets both for D = 128; 4 ((r / 2) % 2) + (r / 4) % 4
+// for D = 64.
 template <int D> __device__ __forceinline__ int bswz(int r) {
-  return D == 128 ? (sigma32(r & 31) & 15) : ((r >> 1) & 7);
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 template <int D> __device__ __forceinline__ int tile_off(int r, int c) {   // element offset of (row, column)
   return r * D + 8 * ((c >> 3) ^ bswz<D>(r)) + (c & 7);
