@@ -240,6 +240,11 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   // K: write i covers rows 8i..8i+7 (16-byte chunk lane%8 of row 8i + lane/8);
   // V^T: write i covers d rows 16i..16i+15 (chunk lane%4 of row 16i + lane/4).
   // The global chunk is XOR-swizzled by the row, so reads below XOR back.
+  // The patterns keep the 16-lane row reads conflict-free on 64 banks x 4
+  // bytes: K rows are 128 bytes (two per 256-byte bank line), so the 8 even
+  // and the 8 odd rows of a read each need 8 distinct patterns: (kr / 2) % 8.
+  // V^T rows are 64 bytes (four per line): rows d, d+4, d+8, d+12 need 4
+  // distinct patterns: (d / 4) % 4.
   auto issue = [&](int tile, int stg) {
     const int kv0 = tile * KT;
 #pragma unroll
@@ -247,10 +252,10 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
       const int i = LPW * wave + i2;
       const int kr = 8 * i + (lane >> 3), kc = lane & 7;
       const int key = min(kv0 + kr, n - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * D8 + 16 * (kc ^ (kr & 7))),
+      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * D8 + 16 * (kc ^ ((kr >> 1) & 7))),
                                        (lds_void8*)(smem + stg * 2 * TILEB + i * 1024), 16, 0, 0);
       const int d = 16 * i + (lane >> 2), vc = lane & 3;
-      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)d * npad + kv0 + 16 * (vc ^ ((d >> 1) & 3))),
+      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)d * npad + kv0 + 16 * (vc ^ ((d >> 2) & 3))),
                                        (lds_void8*)(smem + stg * 2 * TILEB + TILEB + i * 1024), 16, 0, 0);
     }
   };
@@ -286,8 +291,8 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int c0 = 4 * ks + 2 * half;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * (c0 ^ (kr & 7)));
-        const u32x4 c = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * ((c0 + 1) ^ (kr & 7)));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * (c0 ^ ((kr >> 1) & 7)));
+        const u32x4 c = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * ((c0 + 1) ^ ((kr >> 1) & 7)));
         const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
         s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], s[blk], 0, 0, 0, 127, 0, 127);
       }
@@ -354,7 +359,7 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     // O^T += V^T P^T: lane (d = 32 db + lane % 32, half) reads positions 32 half .. +31 of row d
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + r32, sw = (d >> 1) & 3;
+      const int d = 32 * db + r32, sw = (d >> 2) & 3;
       const u32x4 a = *reinterpret_cast<const u32x4*>(vs_ + d * KT + 16 * ((2 * half) ^ sw));
       const u32x4 c = *reinterpret_cast<const u32x4*>(vs_ + d * KT + 16 * ((2 * half + 1) ^ sw));
       const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
