@@ -33,6 +33,7 @@ constexpr int D8 = 128;      // head dim
 constexpr int QB = 128;      // query rows per scale block (and per attention workgroup)
 constexpr int KT = 64;       // keys per scale block and per tile
 constexpr int ST8 = 4;       // K/V tile ring depth (two tiles in flight beyond the two in use)
+constexpr int VROWS = 256;   // V rows per workgroup of the head maximum
 
 #ifndef FA_FP8_WPE
 #define FA_FP8_WPE 2         // waves per SIMD the attention kernel is register-limited to
@@ -83,6 +84,8 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const Fp8QuantParams 
   const int c = tid & 15, rsub = tid >> 4;   // lane's 8-value chunk, row within the pass
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = p.seqlen;
+  if (which == 0 && blk == 0 && h == 0 && b == 0)     // V's maximum accumulates here next
+    for (int i = tid; i < p.batch * p.heads_kv; i += 256) p.v_scale[i] = 0.f;
   const __bf16* src = reinterpret_cast<const __bf16*>(which == 0 ? p.q : p.k);
   const int64_t* st = which == 0 ? p.q_stride : p.kv_stride;
   const int heads = which == 0 ? p.heads_q : p.heads_kv;
@@ -155,54 +158,80 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const Fp8QuantParams 
   }
 }
 
-// Quantise one kv head of V (one scale) into the transposed, key-permuted
-// layout: grid (heads_kv, batch).
-__global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p) {
+// V has one scale per kv head, so its quantisation runs in three steps:
+// the head's absolute maximum (fp8_v_amax_kernel, by atomics on the bit
+// pattern of v_scale: non-negative floats order as unsigned integers; the
+// first workgroup of the Q quantiser, earlier on the stream, zeroes v_scale),
+// the codes (fp8_quant_v_kernel, one workgroup per 64-key tile), and the
+// maximum turned into the scale (fp8_v_scale_kernel).
+__global__ __launch_bounds__(256) void fp8_v_amax_kernel(const Fp8QuantParams p) {
   __shared__ float wmax[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[D8 * KT];     // [d][position]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
-  const __bf16* src = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride[0] + (int64_t)h * p.kv_stride[1];
   const int c = tid & 15, rsub = tid >> 4;   // 16 lanes per row, 8 values each
-
+  const int r0 = blockIdx.x * VROWS, h = blockIdx.y, b = blockIdx.z;
+  const int n = p.seqlen;
+  const __bf16* src = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride[0] + (int64_t)h * p.kv_stride[1];
   float amax = 0.f;
-  for (int row = rsub; row < n; row += 16) {
-    const bf16x8 v = as_bf16x8(load16(src + (int64_t)row * p.kv_stride[2] + 8 * c));
+#pragma unroll 4
+  for (int ps = 0; ps < VROWS / 16; ++ps) {
+    const int row = r0 + ps * 16 + rsub;
+    if (row < n) {
+      const bf16x8 v = as_bf16x8(load16(src + (int64_t)row * p.kv_stride[2] + 8 * c));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+    }
   }
   amax = wave_max(amax);
   if (lane == 0) wmax[wave] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  if (tid == 0) {
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(reinterpret_cast<unsigned*>(p.v_scale) + (int64_t)b * p.heads_kv + h, __float_as_uint(amax));
+  }
+}
+
+// One 64-key tile of one kv head of V into the transposed, key-permuted
+// layout; v_scale holds the head's absolute maximum.
+__global__ __launch_bounds__(256) void fp8_quant_v_kernel(const Fp8QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D8 * KT];     // [d][position]
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * KT, h = blockIdx.y, b = blockIdx.z;
+  const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
+  const __bf16* src = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride[0] + (int64_t)h * p.kv_stride[1];
+  const int c = tid & 15, rsub = tid >> 4;   // 16 lanes per row, 8 values each
+
+  const float amax = p.v_scale[(int64_t)b * p.heads_kv + h];
   const float safe = amax > 0.f ? amax : 448.f;
   const float inv = 448.f / safe;
-  if (tid == 0) p.v_scale[(int64_t)b * p.heads_kv + h] = safe / 448.f;
 
   uint8_t* dst = reinterpret_cast<uint8_t*>(p.v8t) + ((int64_t)b * p.heads_kv + h) * D8 * npad;
-  for (int t0 = 0; t0 < npad; t0 += KT) {
-    __syncthreads();                         // the previous tile's readers are done
 #pragma unroll
-    for (int ps = 0; ps < KT / 16; ++ps) {
-      const int kappa = ps * 16 + rsub, row = t0 + kappa;
-      const bf16x8 v = as_bf16x8(row < n ? load16(src + (int64_t)row * p.kv_stride[2] + 8 * c) : u32x4{0, 0, 0, 0});
-      const int pos = vpos(kappa);
+  for (int ps = 0; ps < KT / 16; ++ps) {
+    const int kappa = ps * 16 + rsub, row = t0 + kappa;
+    const bf16x8 v = as_bf16x8(row < n ? load16(src + (int64_t)row * p.kv_stride[2] + 8 * c) : u32x4{0, 0, 0, 0});
+    const int pos = vpos(kappa);
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int w = pack2<false>(clamp448((float)v[e] * inv), clamp448((float)v[e + 1] * inv), 0);
-        tile[(8 * c + e) * KT + pos] = (uint8_t)(w & 0xff);
-        tile[(8 * c + e + 1) * KT + pos] = (uint8_t)((w >> 8) & 0xff);
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const int w = pack2<false>(clamp448((float)v[e] * inv), clamp448((float)v[e + 1] * inv), 0);
+      tile[(8 * c + e) * KT + pos] = (uint8_t)(w & 0xff);
+      tile[(8 * c + e + 1) * KT + pos] = (uint8_t)((w >> 8) & 0xff);
     }
-    __syncthreads();
-    // 128 rows x 64 bytes out: 16 bytes per thread, two rounds
+  }
+  __syncthreads();
+  // 128 rows x 64 bytes out: 16 bytes per thread, two rounds
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i, d = idx >> 2, ch = idx & 3;
-      *reinterpret_cast<u32x4*>(dst + (int64_t)d * npad + t0 + 16 * ch) =
-          *reinterpret_cast<const u32x4*>(tile + d * KT + 16 * ch);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, d = idx >> 2, ch = idx & 3;
+    *reinterpret_cast<u32x4*>(dst + (int64_t)d * npad + t0 + 16 * ch) =
+        *reinterpret_cast<const u32x4*>(tile + d * KT + 16 * ch);
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_v_scale_kernel(const Fp8QuantParams p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < p.batch * p.heads_kv) {
+    const float amax = p.v_scale[i];
+    p.v_scale[i] = (amax > 0.f ? amax : 448.f) / 448.f;
   }
 }
 
@@ -428,7 +457,18 @@ hipError_t launch_fp8_quant(const Fp8QuantParams& p, hipStream_t stream) {
                      stream, p, 1);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(detail::fp8_quant_v_kernel, dim3((unsigned)p.heads_kv, (unsigned)p.batch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(detail::fp8_v_amax_kernel,
+                     dim3((unsigned)((p.seqlen + VROWS - 1) / VROWS), (unsigned)p.heads_kv, (unsigned)p.batch), dim3(256),
+                     0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(detail::fp8_quant_v_kernel,
+                     dim3((unsigned)((p.seqlen + KT - 1) / KT), (unsigned)p.heads_kv, (unsigned)p.batch), dim3(256), 0,
+                     stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(detail::fp8_v_scale_kernel, dim3((unsigned)((p.batch * p.heads_kv + 255) / 256)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
