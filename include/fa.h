@@ -302,7 +302,8 @@ FA_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const voi
  *            V transposed; inside every 64-key tile key kappa sits at position
  *            32 ((kappa / 4) % 2) + 16 (kappa / 32) + 4 ((kappa % 32) / 8) + kappa % 4;
  *            padding keys are zero
- *   v_scale  [batch, heads_kv] float32
+ *   v_scale  [batch, heads_kv] float32 (while the call's kernels run on the
+ *            stream it holds V's running maximum: read it after them)
  * Supported: head_dim 128; heads_q % heads_kv == 0; 16-byte aligned tensors;
  * strides multiples of 8 elements. Otherwise FA_ERR_UNSUPPORTED.
  */
