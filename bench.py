@@ -449,6 +449,76 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, cmd_fetch: str, cmd_
     print(json.dumps(d, indent=2))
 
 
+MOPS_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+MOPS_FLOPS = 512              # FLOPs per unit of the SQ_INSTS_VALU_MFMA_MOPS_* counters
+
+
+def phase_flops():
+    """Algorithmic FLOPs per launch of each bench phase that runs on the
+    matrix cores, counted as in the bench line (4 d per visible pair; the
+    backward's five products). Decode, priced in bytes, is listed as 4 Hq d
+    per cached token for the counter cross-check."""
+    from io_aware_flashattention_amd import cost_model as cm
+    from io_aware_flashattention_amd import workloads as W
+    pc = W.CONFIGS["c4a_gqa_8k"]
+    pre = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)
+    out = {"prefill c4a (step)": pre, "prefill c4a (backward inputs)": pre, "fp8 fwd_fp8_kernel": pre,
+           "backward (dK/dV + dQ)": cm.backward_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)}
+    for label, name in (("prefill window c7", "c7_window_8k"), ("prefill varlen c6", "c6_varlen_causal")):
+        vc = W.VARLEN_CONFIGS[name]
+        vl = W.varlen_lengths(vc)
+        if vc.window >= 0:
+            out[label] = sum(cm.window_flops(vc.heads_q, int(n), vc.head_dim, vc.window) for n in vl)
+        else:
+            out[label] = cm.varlen_flops(vl, vc.heads_q, vc.head_dim, vc.causal)
+    dc = W.DECODE_CONFIGS["c5_decode"]
+    dec = 4 * dc.heads_q * dc.head_dim * int(W.decode_lengths(dc).sum())   # q K^T and P V per cached token
+    out["decode split (step)"] = out["paged decode split"] = dec
+    return out
+
+
+def summarize_mops(d: str, out: str, cmd: str, n_launch: int):
+    """rocprofv3 --pmc run of this bench with the MFMA-op counters -> FLOPs the
+    matrix cores executed per launch of each phase, beside the algorithmic
+    count. Executed >= algorithmic; the excess is masked work on diagonal and
+    ragged tiles, the weight-sum products, (backward) S and dP computed in
+    both kernels, and (decode) the 24 of 32 matrix columns that one kv head's
+    8 query rows leave empty."""
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        sys.exit(f"no counter_collection.csv under {d}")
+    rows = _read_csv(files[0])
+    flops = {}
+    for counter in MOPS_COUNTERS:               # one row per dispatch and counter: label each counter apart
+        per = {}
+        for label, r in _dispatch_labels([r for r in rows if r.get("Counter_Name") == counter], "Kernel_Name",
+                                         n_launch):
+            if label is None:
+                continue
+            key = "backward (dK/dV + dQ)" if label.startswith(("backward bwd_dkdv", "backward bwd_dq")) else label
+            per.setdefault(key, {}).setdefault(label, []).append(float(r["Counter_Value"]))
+        for key, parts in per.items():           # average over launches, summed over a phase's kernels
+            flops.setdefault(key, {})[counter] = sum(sum(x) / len(x) for x in parts.values()) * MOPS_FLOPS
+    alg = phase_flops()
+    lines = ["# MFMA work executed per launch (rocprofv3 counters)", "", f"command: `{cmd}`", "",
+             f"kernel sources: {sources_hash()}", "",
+             f"FLOPs = counter x {MOPS_FLOPS}, averaged over a phase's launches; algorithmic FLOPs as in the bench line.",
+             "", "| phase | bf16 MFMA FLOPs | fp8 MFMA FLOPs | fp4 MFMA FLOPs | algorithmic FLOPs | executed / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    for label in sorted(flops):
+        f = flops[label]
+        ex = sum(f.values())
+        a = alg.get(label)
+        ratio = f"{ex / a:.3f}" if a else "—"
+        lines.append(f"| {label} | {f.get(MOPS_COUNTERS[0], 0):.4g} | {f.get(MOPS_COUNTERS[1], 0):.4g} | "
+                     f"{f.get(MOPS_COUNTERS[2], 0):.4g} | {a:.4g} | {ratio} |" if a else
+                     f"| {label} | {f.get(MOPS_COUNTERS[0], 0):.4g} | {f.get(MOPS_COUNTERS[1], 0):.4g} | "
+                     f"{f.get(MOPS_COUNTERS[2], 0):.4g} | — | — |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,12 +528,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mops", metavar="DIR")
     ap.add_argument("--cmd", nargs="*", default=[], help="commands recorded in a summary")
     ap.add_argument("--out")
     args = ap.parse_args()
     n_launch = args.warmup + args.steps       # launches per bench phase of the profiled run
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args.out, " ".join(args.cmd), n_launch, args.steps)
+    if args.summarize_mops:
+        return summarize_mops(args.summarize_mops, args.out, " ".join(args.cmd), n_launch)
     if args.summarize_pmc:
         cmds = args.cmd + ["", ""]
         return summarize_pmc(*args.summarize_pmc, args.out, cmds[0], cmds[1], n_launch)
