@@ -55,6 +55,9 @@
 #ifndef FA_FWD_PRIO
 #define FA_FWD_PRIO 0        // raise wave priority during matrix-core units
 #endif
+#ifndef FA_FWD_DMA_SPLIT
+#define FA_FWD_DMA_SPLIT 1   // each group issues its K/V loads in its own softmax phase
+#endif
 #ifndef FA_FWD_AHEAD
 #define FA_FWD_AHEAD 4       // fragment-read steps issued ahead of their MFMA
 #endif
@@ -809,10 +812,22 @@ void fwd_pp_kernel(const FwdParams p) {
   const int nunits = 2 * ntiles + 1;              // G(-1), S(0), G(0), ..., S(nt-1), G(nt-1)
   const int nph = nunits + 1;
   auto phase_begin = [&](int ph) {
+#if FA_FWD_DMA_SPLIT
+    // each wave issues its share of tile tt + STAGES in its own softmax
+    // phase, off the matrix-core units: group 1 at phase 2tt+4, group 0 one
+    // phase later. At every odd phase's end both groups have issued the same
+    // tiles, so the waits below are unchanged.
+    const int pg = ph - 4 - (grp == 0 ? 1 : 0);
+    if (pg >= 0 && !(pg & 1)) {
+      const int tt = pg >> 1;
+      if (tt + STAGES < ntiles) issue(tt + STAGES, tt % STAGES);
+    }
+#else
     if (ph >= 4 && !(ph & 1)) {
       const int tt = (ph - 4) >> 1;
       if (tt + STAGES < ntiles) issue(tt + STAGES, tt % STAGES);
     }
+#endif
   };
   auto phase_end = [&](int ph) {
     if (ph + 1 >= nph) return;
