@@ -36,6 +36,14 @@ constexpr int NWB = 4;       // waves per workgroup
 #endif
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // 16-byte chunk swizzle of a tile row (any XOR pattern is correct as long as
 // every access of row r uses this row's value). It depends on r % 16 only,
@@ -237,16 +245,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
 }
 
 // dK and dV for 128 keys of one (batch, kv head), walking the query rows 64
-// at a time (two 32-row blocks) with the next 64 rows prefetched. Under the
-// causal mask key tile t sees the rows from 128 t on, so a workgroup takes
-// tiles t and T-1-t in turn and every workgroup does the same amount of work.
+// at a time (two 32-row blocks). Under the causal mask key tile t sees the
+// rows from 128 t on, so a workgroup takes tiles t and T-1-t in turn and
+// every workgroup does the same amount of work.
+// Q and dO tiles reach LDS by direct global -> LDS loads into a three-stage
+// ring, two steps ahead, with one barrier per step. Rows past the end are
+// clamped to the last row: their LSE slot is set to +inf, so their weights
+// are 0. LSE and D come in by 4-byte loads (waves 0 and 1), which then put
+// LSE in base 2 and set the slots past the end before the barrier.
 template <int D, bool CAUSAL, typename TOut>
 __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, RB = 2 * BB;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[RB * D];
-  __shared__ __attribute__((aligned(16))) __bf16 gs[RB * D];      // dO
-  __shared__ __attribute__((aligned(16))) float ls[RB];           // LSE * log2(e) (+inf past the end)
-  __shared__ __attribute__((aligned(16))) float ds[RB];           // D
+  constexpr int TILE = RB * D;               // elements of one Q or dO tile
+  constexpr int LPW = TILE * 2 / 1024 / NWB; // 1-KB loads per wave and tensor
+  constexpr int RPL = 1024 / (2 * D);        // rows per 1-KB load
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NST = 3;                     // ring depth
+  static_assert(TILE * 2 % (1024 * NWB) == 0 && RB == 64, "");
+  __shared__ __attribute__((aligned(16))) __bf16 ring[NST][2][TILE];    // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lring[NST][2][RB];      // [stage][LSE log2 e, D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int ktiles = (p.seqlen_k + NWB * BB - 1) / (NWB * BB);
@@ -258,8 +275,16 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
   const float c2 = p.scale_log2;
   const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
   const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_stride[0] + kvh * p.kv_stride[1];
-  Prefetch<D, RB> pq, pg;
-  float pl = 0.f, pd = 0.f;
+  const int64_t rs = p.q_stride[2];
+  // this lane's row and source chunk in each of its loads: LDS chunk slot
+  // lane % CPR of row r holds the row's logical chunk slot ^ bswz(r)
+  int drow[LPW], dchk[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * RPL + lane / CPR;
+    drow[i] = r;
+    dchk[i] = 8 * ((lane % CPR) ^ bswz<D>(r));
+  }
 
   for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
     const int kt = pass == 0 ? u : ktiles - 1 - u;
@@ -280,31 +305,54 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
     const int r_begin = CAUSAL ? k0 : 0;     // earlier rows see none of these keys
     const int nblk = (nq - r_begin + RB - 1) / RB;
     const int total = p.group * nblk;        // (query head, row block) steps
-    auto fetch = [&](int step) {
+    auto issue = [&](int step, int st) {
       const int g = step / nblk, r0 = r_begin + (step % nblk) * RB;
       const int hq = kvh * p.group + g;
       const int64_t qo = (int64_t)b * p.q_stride[0] + (int64_t)hq * p.q_stride[1];
-      pq.load(reinterpret_cast<const __bf16*>(p.q) + qo, p.q_stride[2], r0, nq, tid);
-      pg.load(reinterpret_cast<const __bf16*>(p.dout) + qo, p.q_stride[2], r0, nq, tid);
-      if (tid < RB) {
-        const int64_t so = ((int64_t)b * p.heads_q + hq) * nq;
-        const int r = r0 + tid;
-        pl = r < nq ? p.lse[so + r] * kLog2e : __builtin_huge_valf();
-        pd = r < nq ? p.dsum[so + r] : 0.f;
+      const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + qo;
+      const __bf16* gb = reinterpret_cast<const __bf16*>(p.dout) + qo;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int64_t e = (int64_t)min(r0 + drow[i], nq - 1) * rs + dchk[i];
+        __builtin_amdgcn_global_load_lds((const void*)(qb + e), (lds_void*)&ring[st][0][(wave * LPW + i) * 512], 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)(gb + e), (lds_void*)&ring[st][1][(wave * LPW + i) * 512], 16, 0,
+                                         0);
+      }
+      if (wave < 2) {
+        const int64_t so = ((int64_t)b * p.heads_q + hq) * nq + min(r0 + lane, nq - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(wave == 0 ? p.lse + so : p.dsum + so),
+                                         (lds_void*)&lring[st][wave][0], 4, 0, 0);
       }
     };
-    if (total > 0) fetch(0);
+    // every wave waits for its own loads of this step's tile (the next tile's may fly)
+    auto wait_tile = [&](bool next_in_flight) {
+      if (!next_in_flight) wait_vmcnt<0>();
+      else if (wave < 2) wait_vmcnt<2 * LPW + 1>();
+      else wait_vmcnt<2 * LPW>();
+    };
+
+    __syncthreads();                         // the previous pass's readers are done with the ring
+    if (total > 0) issue(0, 0);
+    if (total > 1) issue(1, 1);
     for (int step = 0; step < total; ++step) {
+      const int st = step % NST;
       const int r0 = r_begin + (step % nblk) * RB;
-      __syncthreads();                       // the previous step's readers are done
-      pq.store(qs, tid);
-      pg.store(gs, tid);
-      if (tid < RB) {
-        ls[tid] = pl;
-        ds[tid] = pd;
+      wait_tile(step + 1 < total);
+      if (wave < 2) {                        // LSE in base 2; rows past the end: LSE +inf, D 0
+        float* x = &lring[st][wave][lane];
+        const float v = *x;
+        *x = r0 + lane < nq ? (wave == 0 ? v * kLog2e : v) : (wave == 0 ? __builtin_huge_valf() : 0.f);
       }
-      __syncthreads();
-      if (step + 1 < total) fetch(step + 1); // in flight during this step's matrix work
+      // tile `step` is published; the stage of step-1 is free for step+2
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 2 < total) issue(step + 2, (step + 2) % NST);
+      const __bf16* qs = ring[st][0];
+      const __bf16* gs = ring[st][1];
+      const float* ls = lring[st][0];
+      const float* ds = lring[st][1];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int rs0 = r0 + sb * BB;
