@@ -15,8 +15,8 @@
 //         it takes key tiles t and T-1-t so every workgroup has equal work;
 //   dq:   a workgroup owns 128 query rows of one head (32 per wave) and walks
 //         the key tiles, accumulating dQ in registers.
-// Both stream their operand tiles 64 rows at a time through LDS, the next 64
-// rows held in registers while the current ones feed the matrix cores.
+// Both stream their operand tiles 64 rows at a time through LDS by direct
+// global -> LDS loads, issued a step or two before the matrix work reads them.
 // Each of the five products runs on v_mfma_f32_32x32x16_bf16. Operand tiles
 // are staged in LDS and read two ways: 16-byte row fragments in sigma order
 // (so the score accumulator comes out in the B-operand layout of the next
@@ -65,33 +65,6 @@ template <int D> __device__ __forceinline__ int bswz(int r) {
 template <int D> __device__ __forceinline__ int tile_off(int r, int c) {   // element offset of (row, column)
   return r * D + 8 * ((c >> 3) ^ bswz<D>(r)) + (c & 7);
 }
-
-// Rows [r0, r0 + ROWS) of a row-major global matrix (row stride rs
-// elements) held in registers on their way to a ROWS x D LDS tile: load()
-// issues the global reads (rows at or past `rows` are zero) early, store()
-// writes them to LDS once the tile's previous readers are done, so the
-// global latency hides behind a block of matrix work.
-template <int D, int ROWS>
-struct Prefetch {
-  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
-  static constexpr int N = ROWS * CPR / (NWB * 64);       // per thread
-  static_assert(ROWS * CPR % (NWB * 64) == 0, "");
-  u32x4 v[N];
-  __device__ __forceinline__ void load(const __bf16* g, int64_t rs, int r0, int rows, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + NWB * 64 * i, r = idx / CPR, c = idx % CPR;
-      v[i] = r0 + r < rows ? load16(g + (int64_t)(r0 + r) * rs + 8 * c) : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* t, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + NWB * 64 * i, r = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<u32x4*>(t + tile_off<D>(r, 8 * c)) = v[i];
-    }
-  }
-};
 
 // A operand of X Y^T with X a 32-row LDS tile read in sigma order: lane l
 // gets row sigma(l % 32), elements 16 kc + 8 (l / 32) .. +7.
@@ -378,16 +351,20 @@ __global__ __launch_bounds__(NWB * 64) void bwd_dkdv_kernel(const BwdParams p) {
 }
 
 // dQ for 128 query rows of one (batch, query head), walking the keys 64 at a
-// time (two 32-key blocks) with the next 64 prefetched. Under the causal
-// mask the heaviest query tiles are dispatched first.
+// time (two 32-key blocks) with the next 64 in flight. Under the causal mask
+// the heaviest query tiles are dispatched first.
 // (Capped at two waves per SIMD: 256 registers hold it without spills, and
 // the second wave's matrix work overlaps this one's softmax.)
 template <int D, bool CAUSAL, typename TOut>
 __global__ __launch_bounds__(NWB * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, KB2 = 2 * BB;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[KB2 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[KB2 * D];
+  constexpr int TILE = KB2 * D;              // elements of one K or V tile
+  constexpr int LPW = TILE * 2 / 1024 / NWB; // 1-KB loads per wave and tensor
+  constexpr int RPL = 1024 / (2 * D);        // rows per 1-KB load
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static_assert(TILE * 2 % (1024 * NWB) == 0, "");
+  __shared__ __attribute__((aligned(16))) __bf16 ring[2][2][TILE];     // [stage][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int qtiles = (p.seqlen_q + NWB * BB - 1) / (NWB * BB);
@@ -421,20 +398,35 @@ void bwd_dq_kernel(const BwdParams p) {
 
   const float c2 = p.scale_log2;
   const int k_end = CAUSAL ? min(nk, q0 + NWB * BB) : nk;
-  Prefetch<D, KB2> pk, pv;
-  if (0 < k_end) {
-    pk.load(kp, p.kv_stride[2], 0, nk, tid);
-    pv.load(vp, p.kv_stride[2], 0, nk, tid);
+  // K and V tiles by direct global -> LDS loads into a two-stage ring: tile
+  // t+1 is issued right after the barrier that opens tile t. Keys past the
+  // end are clamped to the last key; the mask removes them.
+  int drow[LPW], dchk[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * RPL + lane / CPR;
+    drow[i] = r;
+    dchk[i] = 8 * ((lane % CPR) ^ bswz<D>(r));
   }
-  for (int kv0 = 0; kv0 < k_end; kv0 += KB2) {
-    __syncthreads();
-    pk.store(ks, tid);
-    pv.store(vs, tid);
-    __syncthreads();
-    if (kv0 + KB2 < k_end) {                 // in flight during this block's matrix work
-      pk.load(kp, p.kv_stride[2], kv0 + KB2, nk, tid);
-      pv.load(vp, p.kv_stride[2], kv0 + KB2, nk, tid);
+  auto issue = [&](int kv0, int st) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int64_t e = (int64_t)min(kv0 + drow[i], nk - 1) * p.kv_stride[2] + dchk[i];
+      __builtin_amdgcn_global_load_lds((const void*)(kp + e), (lds_void*)&ring[st][0][(wave * LPW + i) * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + e), (lds_void*)&ring[st][1][(wave * LPW + i) * 512], 16, 0, 0);
     }
+  };
+  const int nt = (k_end + KB2 - 1) / KB2;
+  if (nt > 0) issue(0, 0);
+  for (int t = 0; t < nt; ++t) {
+    const int kv0 = t * KB2, st = t & 1;
+    wait_vmcnt<0>();                         // this wave's loads of tile t
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // tile t published; tile t-1's stage free
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nt) issue(kv0 + KB2, st ^ 1);   // in flight during this tile's matrix work
+    const __bf16* ks = ring[st][0];
+    const __bf16* vs = ring[st][1];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int kb0 = kv0 + sb * BB;
