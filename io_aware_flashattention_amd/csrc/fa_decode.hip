@@ -90,9 +90,11 @@ __device__ __forceinline__ int64_t range_tokens(const DecodeParams& p, int64_t T
 }
 
 // Position in the token stream: slab (b, kvh), key position inside the slab
-// and end of the current piece (exclusive, inside the slab).
+// (a multiple of the block, so blocks line up with pages), the piece's first
+// key (keys of the first block before it belong to the previous range and
+// are masked) and end of the piece (exclusive, inside the slab).
 struct Cursor {
-  int b, kvh, pos, end;
+  int b, kvh, pos, start, end;
   int64_t slab_off;          // stream offset of the slab's first token
 };
 
@@ -145,7 +147,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     cur.b = b;
     cur.kvh = kvh;
     cur.slab_off = off + (int64_t)kvh * L;
-    cur.pos = (int)(r0 - cur.slab_off);
+    cur.start = (int)(r0 - cur.slab_off);
+    cur.pos = cur.start / KB * KB;
     cur.end = (int)min((int64_t)L, r1 - cur.slab_off);
   }
   // one block further along the range; false once it is exhausted
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       } while (L == 0);
     }
     c.pos = 0;
+    c.start = 0;
     c.end = (int)min((int64_t)L, r1 - c.slab_off);
     return true;
   };
@@ -170,6 +174,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   // ---- DMA of one block: eight 1-KB writes per operand, rows past the piece clamped
   const int drow = lane >> 4;                  // row of the lane's chunk, + 4 per write
   const int dchunk = lane & 15;
+  // byte offsets of the lane's K and V chunks in write i, from the block's
+  // first row (page-aligned paged blocks)
+  const bool fast_pages = PAGED && (p.page_size == 16 || p.page_size % KB == 0);
+  uint32_t lane_k[8], lane_v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + drow;
+    lane_k[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ kswz_d(r))));
+    lane_v[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ vswz_d(r))));
+  }
   // Paged cache: table entries of the block at cursor c (scalar loads through
   // the constant address space; ids outside [0, num_pages) are clamped).
   auto pages_of = [&](const Cursor& c) {
@@ -193,6 +207,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     const __bf16* vp = reinterpret_cast<const __bf16*>(p.v);
     __bf16* dst = smem + st * 2 * BLK;
     if constexpr (PAGED) {
+      if (fast_pages && c.pos + KB <= c.end) {
+        // a whole, page-aligned block: rows 0-15 and 16-31 sit in pages e0 and
+        // e1 (16-slot pages), or all in e0 from slot off (pages of 32k slots);
+        // each load is a wave-uniform base plus the lane's precomputed offset.
+        // A piece's last block takes the clamped path below: a masked key has
+        // weight 0, but 0 times a never-written V slot can still be NaN.
+        const int top = p.num_pages - 1;
+        const int64_t hofs = (int64_t)c.kvh * p.kv_stride[1];
+        const int rs = (int)p.kv_stride[2];
+        const char* b0 = reinterpret_cast<const char*>(
+            kp + (int64_t)min(max(pr.e0, 0), top) * p.kv_stride[0] + hofs + (p.page_size == 16 ? 0 : pr.off * rs));
+        const char* b1 = p.page_size == 16
+            ? reinterpret_cast<const char*>(kp + (int64_t)min(max(pr.e1, 0), top) * p.kv_stride[0] + hofs) - 32 * rs
+            : b0;
+        asm("" : "+s"(b0), "+s"(b1));
+        const intptr_t dvk = reinterpret_cast<intptr_t>(vp) - reinterpret_cast<intptr_t>(kp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const char* base = i < 4 ? b0 : b1;
+          __builtin_amdgcn_global_load_lds((const void*)(base + lane_k[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(base + dvk + lane_v[i]), (lds_void*)(dst + BLK + i * 512),
+                                           16, 0, 0);
+        }
+        return;
+      }
       // wave-uniform (page, kv head) bases of the block's pages; each lane then
       // picks its row's page with two compares and adds slot * row stride
       // (32-bit: page_size * stride < 2^31 is checked on the host)
@@ -305,10 +344,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
     for (int kc = 0; kc < KSTEPS; ++kc)
       sc = mfma32(*reinterpret_cast<const bf16x8*>(ks + koff[kc]), qf[kc], sc);
-    const int valid = cur.end - cur.pos;       // keys of this block inside the piece
-    if (valid < KB) {
+    const int valid = cur.end - cur.pos;       // keys of this block inside the piece: [lo, valid)
+    const int lo = cur.start - cur.pos;
+    if (valid < KB || lo > 0) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) sc[jj] = acc_key(jj, half) >= valid ? kNegInf : sc[jj];
+      for (int jj = 0; jj < 16; ++jj) {
+        const int kk = acc_key(jj, half);
+        sc[jj] = (kk >= valid) | (kk < lo) ? kNegInf : sc[jj];
+      }
     }
     float mx = sc[0];
 #pragma unroll
