@@ -175,8 +175,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int drow = lane >> 4;                  // row of the lane's chunk, + 4 per write
   const int dchunk = lane & 15;
   // byte offsets of the lane's K and V chunks in write i, from the block's
-  // first row (page-aligned paged blocks)
-  const bool fast_pages = PAGED && (p.page_size == 16 || p.page_size % KB == 0);
+  // first row (whole blocks: contiguous, or page-aligned paged)
+  // (32-bit: usable while 32 rows of the row or slot stride stay below 2^31 bytes)
+  const bool lane_ok = p.kv_stride[2] < (int64_t(1) << 25);
+  const bool fast_pages = PAGED && lane_ok && (p.page_size == 16 || p.page_size % KB == 0);
   uint32_t lane_k[8], lane_v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -262,6 +264,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
                                          (lds_void*)(dst + BLK + i * 512), 16, 0, 0);
       }
     } else {
+      if (lane_ok && c.pos + KB <= c.end) {    // a whole block: a uniform base plus the lane offsets
+        const char* b0 = reinterpret_cast<const char*>(
+            kp + (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1] + (int64_t)c.pos * p.kv_stride[2]);
+        asm("" : "+s"(b0));
+        const intptr_t dvk = reinterpret_cast<intptr_t>(vp) - reinterpret_cast<intptr_t>(kp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_global_load_lds((const void*)(b0 + lane_k[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(b0 + dvk + lane_v[i]), (lds_void*)(dst + BLK + i * 512), 16,
+                                           0, 0);
+        }
+        return;
+      }
       const int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
       const int last = c.end - 1;
 #pragma unroll
