@@ -103,3 +103,45 @@ def test_small_lengths_and_edges():
             ro, rl = attention_ref(W.to_f64(q[b])[None, :, None, :], W.to_f64(kc[b:b + 1, :, :n]),
                                    W.to_f64(vc[b:b + 1, :, :n]), cfg.scale)
             check(o[b], l[b], ro[0, :, 0], rl[0, :, 0], f"edges b={b} L={n} split={split}")
+
+
+def test_huge_row_stride_takes_the_general_path():
+    """Whole blocks load from one base plus 32-bit per-lane offsets over 32
+    rows; a row (or page-slot) stride of 2^25 elements is past what those
+    offsets hold, so these calls must take the clamped general path and still
+    match the oracle. (About 12 GB of strided cache.)"""
+    import gc
+    d, L, stride = 128, 45, 1 << 25
+    cfg = W.DecodeConfig("huge_stride", 1, 8, 1, 1, L, d, 79)
+    q, kc, vc, _ = W.make_decode_inputs(cfg, pad="zero", lengths=np.array([L], dtype=np.int32))
+    ro, rl = attention_ref(W.to_f64(q[0])[None, :, None, :], W.to_f64(kc), W.to_f64(vc), cfg.scale)
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    say(f"case decode row stride {stride} elements, L={L}")
+    bufs = []
+    for x in (kc, vc):
+        buf = torch.zeros((L, stride), dtype=torch.bfloat16, device="cuda")
+        buf[:, :d] = to_dev(x)[0, 0]
+        bufs.append(buf)
+    k, v = (b.as_strided((1, 1, L, d), (L * stride, L * stride, stride, 1)) for b in bufs)
+    o, l = fa().decode(to_dev(q), k, v, lens, scale=cfg.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(o.cpu().numpy()[0], l.cpu().numpy()[0], ro[0, :, 0], rl[0, :, 0], "decode, huge row stride")
+    del k, v, bufs
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    say(f"case paged decode slot stride {stride} elements, 16-slot pages")
+    ps = 16
+    npg = -(-L // ps)
+    pools = []
+    for x in (kc, vc):
+        pool = torch.zeros((npg * ps, stride), dtype=torch.bfloat16, device="cuda")   # page p, slot s at row p*ps+s
+        pool[:L, :d] = to_dev(x)[0, 0]
+        pools.append(pool.as_strided((npg, 1, ps, d), (ps * stride, ps * stride, stride, 1)))
+    table = torch.arange(npg, dtype=torch.int32, device="cuda")[None]
+    o, l = fa().decode_paged(to_dev(q), pools[0], pools[1], table, lens, scale=cfg.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(o.cpu().numpy()[0], l.cpu().numpy()[0], ro[0, :, 0], rl[0, :, 0], "paged decode, huge slot stride")
+    del pools
+    gc.collect()
+    torch.cuda.empty_cache()
