@@ -274,17 +274,33 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   // and the 8 odd rows of a read each need 8 distinct patterns: (kr / 2) % 8.
   // V^T rows are 64 bytes (four per line): rows d, d+4, d+8, d+12 need 4
   // distinct patterns: (d / 4) % 4.
+  // lane offsets of its chunks from the tile's first key (K) and first position (V^T)
+  int koff[LPW];
+  int64_t voff[LPW];
+#pragma unroll
+  for (int i2 = 0; i2 < LPW; ++i2) {
+    const int i = LPW * wave + i2;
+    const int kr = 8 * i + (lane >> 3), kc = lane & 7;
+    koff[i2] = kr * D8 + 16 * (kc ^ ((kr >> 1) & 7));
+    const int d = 16 * i + (lane >> 2), vc = lane & 3;
+    voff[i2] = (int64_t)d * npad + 16 * (vc ^ ((d >> 2) & 3));
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // LDS destinations stay scalar
   auto issue = [&](int tile, int stg) {
     const int kv0 = tile * KT;
+    const uint8_t* vb = vp + kv0;            // V^T is zero-padded to npad positions: no clamp
+    const bool whole = kv0 + KT <= n;        // else the last keys repeat key n-1
+    const uint8_t* kb = kp + (int64_t)kv0 * D8;
 #pragma unroll
     for (int i2 = 0; i2 < LPW; ++i2) {
-      const int i = LPW * wave + i2;
-      const int kr = 8 * i + (lane >> 3), kc = lane & 7;
-      const int key = min(kv0 + kr, n - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + (int64_t)key * D8 + 16 * (kc ^ ((kr >> 1) & 7))),
-                                       (lds_void8*)(smem + stg * 2 * TILEB + i * 1024), 16, 0, 0);
-      const int d = 16 * i + (lane >> 2), vc = lane & 3;
-      __builtin_amdgcn_global_load_lds((const void*)(vp + (int64_t)d * npad + kv0 + 16 * (vc ^ ((d >> 2) & 3))),
+      const int i = LPW * wave_u + i2;
+      const uint8_t* ka = kb + koff[i2];
+      if (!whole) {
+        const int kr = 8 * i + (lane >> 3), kc = lane & 7;
+        ka = kp + (int64_t)min(kv0 + kr, n - 1) * D8 + 16 * (kc ^ ((kr >> 1) & 7));
+      }
+      __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void8*)(smem + stg * 2 * TILEB + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + voff[i2]),
                                        (lds_void8*)(smem + stg * 2 * TILEB + TILEB + i * 1024), 16, 0, 0);
     }
   };
