@@ -18,10 +18,13 @@
 // 32-key blocks of two k-steps, the softmax in float32 with the tile's
 // q-scale x k-scale folded into the one FMA per score, and O^T += V^T P^T
 // with P quantised to e4m3 as 2^8 * 2^(x - m) against an integer base m that
-// moves with the row maximum (one FMA and one exponential per score) (so every rescale is an exact power of two and
-// every weight keeps three mantissa bits down to 2^-14 of the largest). O is
-// divided by the sum of the quantised weights (one more MFMA against a row of
-// ones) and multiplied by V's scale; the LSE uses the float32 sum.
+// moves with the row maximum (one FMA and one exponential per score; every
+// rescale is an exact power of two and every weight keeps three mantissa bits
+// down to 2^-14 of the largest). O is divided by the sum of the quantised
+// weights (one more MFMA, against an fp4 operand of ones) and multiplied by
+// V's scale; the LSE uses the float32 sum. Each wave issues the score MFMAs
+// of tile j+1 before the softmax of tile j, so the matrix cores run during
+// the vector work; tiles arrive through a four-stage LDS ring.
 #include "fa_device.h"
 #include "fa_launch.h"
 
