@@ -81,6 +81,13 @@ __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
   return min(max(((const const_i32*)p.seqlens)[b], 0), p.max_seqlen);
 }
 
+// a wave-uniform 64-bit value computed in vector registers, moved to scalar ones
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Tokens per wave range, identical in both kernels: at least split_tokens, a
 // multiple of the block, and W ranges cover all T tokens of the stream.
 __device__ __forceinline__ int64_t range_tokens(const DecodeParams& p, int64_t T) {
@@ -124,24 +131,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int G = p.group;
   const int Hkv = p.heads_kv;
 
-  // ---- plan: stream length and this wave's range [r0, r1)
+  // ---- plan: stream length and this wave's range [r0, r1). The lanes read
+  // the lengths (clamped as seq_len does) and the wave combines them, rather
+  // than one chain of scalar loads per batch.
   int64_t T = 0;
-  for (int b = 0; b < p.batch; ++b) T += (int64_t)seq_len(p, b);
-  T *= Hkv;
+  for (int bb = lane; bb < p.batch; bb += 64) T += min(max(p.seqlens[bb], 0), p.max_seqlen);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) T += __shfl_xor(T, off);
+  T = uniform64(T) * Hkv;
   const int64_t P = range_tokens(p, T);
   const int64_t r0 = (int64_t)w * P;
   if (r0 >= T) return;
   const int64_t r1 = r0 + P < T ? r0 + P : T;
 
-  Cursor cur;                                // slab holding r0
+  Cursor cur;                                // slab holding r0: the first batch whose tokens end past r0
   {
-    int64_t off = 0;
+    int64_t off = 0;                         // stream offset of batch b's first token
     int b = 0;
-    for (;; ++b) {
-      const int64_t n = (int64_t)seq_len(p, b) * Hkv;
-      if (r0 < off + n) break;
-      off += n;
+    int64_t base = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      const int bb = c0 + lane;
+      const int64_t n = bb < p.batch ? (int64_t)min(max(p.seqlens[bb], 0), p.max_seqlen) * Hkv : 0;
+      int64_t incl = n;                      // inclusive prefix over this chunk
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t t = __shfl_up(incl, d);
+        incl += lane >= d ? t : 0;
+      }
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < p.batch && r0 < base + incl);
+      if (hit != 0) {
+        const int first = __builtin_ctzll(hit);
+        b = c0 + first;
+        off = base + __shfl(incl - n, first);
+        break;
+      }
+      base += __shfl(incl, 63);
     }
+    b = __builtin_amdgcn_readfirstlane(b);
+    off = uniform64(off);
     const int L = seq_len(p, b);
     const int kvh = (int)((r0 - off) / L);
     cur.b = b;
@@ -458,13 +485,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const int hq = (int)(row % p.heads_q);
   const int G = p.group;
   const int kvh = hq / G, g = hq % G;
+  // stream length and this row's slab offset: the lanes read the lengths
+  // (clamped as seq_len does) and the wave adds them up, rather than one
+  // chain of scalar loads per batch
   int64_t T = 0, before = 0;
-  for (int bb = 0; bb < p.batch; ++bb) {
-    const int64_t n = seq_len(p, bb);
-    if (bb < b) before += n;
+  for (int bb = lane; bb < p.batch; bb += 64) {
+    const int64_t n = min(max(p.seqlens[bb], 0), p.max_seqlen);
     T += n;
+    before += bb < b ? n : 0;
   }
-  T *= p.heads_kv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    T += __shfl_xor(T, off);
+    before += __shfl_xor(before, off);
+  }
+  T = uniform64(T) * p.heads_kv;
+  before = uniform64(before);
   const int L = seq_len(p, b);
   TOut* op = reinterpret_cast<TOut*>(p.o) + row * D + 2 * lane;
   if (L == 0) {                                // no key: O = 0, LSE = -inf
