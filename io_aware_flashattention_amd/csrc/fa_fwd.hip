@@ -34,6 +34,8 @@
 //     so two row sums are kept: O is divided by the sum of the bf16-rounded
 //     weights that actually enter P V (an exactly normalised combination of V
 //     rows), and the log-sum-exp uses the float32 sum of the weights.
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -49,14 +51,8 @@
 #ifndef FA_FWD_PPST
 #define FA_FWD_PPST 3        // its K/V ring depth
 #endif
-#ifndef FA_FWD_GRP
-#define FA_FWD_GRP 2         // how waves split into the two ping-pong groups
-#endif
 #ifndef FA_FWD_PRIO
 #define FA_FWD_PRIO 0        // raise wave priority during matrix-core units
-#endif
-#ifndef FA_FWD_DMA_SPLIT
-#define FA_FWD_DMA_SPLIT 1   // each group issues its K/V loads in its own softmax phase
 #endif
 #ifndef FA_FWD_AHEAD
 #define FA_FWD_AHEAD 4       // fragment-read steps issued ahead of their MFMA
@@ -87,6 +83,8 @@ template <int D> __device__ __forceinline__ int kswz_t(int r) {
 template <int D> __device__ __forceinline__ int vswz_t(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
+
+template <int N> struct int_c { static constexpr int value = N; };
 
 // LDS pointer type for the direct global -> LDS loads (the host pass of the
 // compiler needs the address space spelled out).
@@ -513,82 +511,132 @@ void fwd_bf16_kernel(const FwdParams p) {
 // in the order G(-1) S(0) G(0) S(1) G(1) ... . Group 1 runs one unit behind
 // group 0, so in every phase between two barriers one wave of each SIMD feeds
 // the matrix core while the other runs the softmax, and the two swap at the
-// next barrier. The K/V ring holds STAGES tiles: tile t is read in phases
-// 2t .. 2t+3 and its stage is refilled with tile t+STAGES at phase 2t+4.
+// next barrier.
+//
+// A dense batch runs on a persistent grid: one workgroup per compute unit,
+// each with a fixed list of work items, and the K/V tiles of a workgroup's
+// consecutive items form one stream through the ring. Stream tile g sits in
+// stage g % STAGES; within its item (index t there) it is read in phases
+// 2t .. 2t+3, and its stage is refilled with stream tile g+STAGES at phase
+// 2t+4 (group 1) or 2t+5 (group 0), so near an item's end the ring already
+// fills with the next item's first tiles. The next item's query rows go
+// global -> LDS together with its first tile: an item starts with its Q and
+// its first K/V tiles on chip, and no workgroup launch separates two items.
+// A packed batch keeps one item per workgroup and leaves the balancing of its
+// mixed lengths to the hardware dispatcher.
 template <int D, bool CAUSAL, typename TOut, int STAGES>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const FwdParams p) {
   constexpr int NW = 8;
-  constexpr int BRW = 32 * NW;               // query rows per workgroup
+  constexpr int BRW = 32 * NW;               // query rows per item
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = BC * D;
   constexpr int ROWB = 2 * D;
   constexpr int NLD = TILE * 2 / 1024;
-  constexpr int LPW = NLD / NW;
+  constexpr int LPW = NLD / NW;              // 1-KB DMA writes per wave per K or V tile
+  constexpr int QLPW = 32 * ROWB / 1024;     // 1-KB DMA writes per wave for its 32 query rows
+  static_assert(D == 128, "a query row fills one LDS bank line");
   static_assert(NLD % NW == 0, "tile / wave mismatch");
-  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+  static_assert(STAGES == 3, "the unit rounds below are written out for a 3-stage ring");
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE];   // [stage][K, V][TILE]
+  // [stage][K, V][TILE] ring, then [wave][32 rows][D] query rows whose 16-byte
+  // chunks are XOR-ed with row % 16 (conflict-free ds_read_b128 of a column)
+  __shared__ __attribute__((aligned(16))) __bf16 smem[STAGES * 2 * TILE + NW * 32 * D];
+  __bf16* const qsm = smem + STAGES * 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int r32 = lane & 31;
-#if FA_FWD_GRP == 0
-  const int grp = wave >> 2;
-#elif FA_FWD_GRP == 1
-  const int grp = wave & 1;
-#else
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // the two waves that share a SIMD take different groups: each wave reads
-  // its SIMD number and takes a ticket from that SIMD's LDS counter
-  __shared__ int simd_ticket[4];
-  if (tid < 4) simd_ticket[tid] = 0;
-  __syncthreads();
+  // its SIMD number and takes a ticket from that SIMD's LDS counter (kept in
+  // the query area, which is free until the first query load)
   int grp;
   {
+    int* const ticket = reinterpret_cast<int*>(qsm);
+    if (tid < 4) ticket[tid] = 0;
+    __syncthreads();
     const int simd = (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;   // HW_ID bits 5:4
     int tk = 0;
-    if (lane == 0) tk = atomicAdd(&simd_ticket[simd], 1);
+    if (lane == 0) tk = atomicAdd(&ticket[simd], 1);
     grp = __builtin_amdgcn_readfirstlane(tk) & 1;
+    __syncthreads();
   }
-#endif
 
-  int L = work_item(blockIdx.x, gridDim.x, p);
-  if (L < 0) return;                         // padding of the last XCD round (whole workgroup)
-  const int g = L % p.group;
-  L /= p.group;
-  const int t = L % p.n_qtiles;
-  L /= p.n_qtiles;
-  const int kvh = L % p.heads_kv;
-  const int b = L / p.heads_kv;
-  const int hq = kvh * p.group + g;
-  const int qt = CAUSAL ? p.n_qtiles - 1 - t : t;
+  // Work items of this workgroup. Dense: the workgroups of XCD x (blockIdx % 8,
+  // the dispatcher's round-robin) share the contiguous range of the logical
+  // order that work_item gives x, dealt out in a snake (round k left to right
+  // for even k, right to left for odd k). Each (batch, kv head) row of the
+  // logical order lists its query tiles heaviest first, with the query heads
+  // of a kv head side by side, so two consecutive rounds give the workgroups
+  // nearly the same causal cost (the same when a row holds whole pairs of
+  // rounds and a round whole groups of heads).
+  const bool dense = p.cu_seqlens == nullptr;
+  struct Item {
+    int64_t q, k, v, o, lse;                 // element offsets of its (sequence, head)
+    int nq, nk, q0, jbase, ntiles;
+    bool valid;
+  };
+  // (called once per item; its inputs pass through an empty asm statement so
+  // that none of its scalar arithmetic is hoisted out of the loops and kept
+  // live in registers through them; the divisions are multiply-shifts by the
+  // launcher's reciprocals)
+  auto rdiv = [&](int n, int which) __attribute__((always_inline)) {
+    const uint32_t m = p.div_m[which];
+    return m == 0 ? n : (int)(__umulhi((uint32_t)n, m) >> (p.div_s[which] - 1));
+  };
+  auto make_item = [&](int idx) __attribute__((always_inline)) {
+    Item it{};
+    int n = p.n_items, bid = blockIdx.x, nwg = gridDim.x, group = p.group, nqt = p.n_qtiles, hkv = p.heads_kv;
+    asm volatile("" : "+s"(n), "+s"(bid), "+s"(nwg), "+s"(group), "+s"(nqt), "+s"(hkv), "+s"(idx));
+    int L;
+    if (dense) {
+      const int per = n >> 3, rem = n & 7, x = bid & 7;
+      const int nslot = nwg >> 3, slot = bid >> 3;
+      const int pos = idx * nslot + ((idx & 1) ? nslot - 1 - slot : slot);
+      if (pos >= per + (x < rem ? 1 : 0)) return it;
+      L = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + pos;
+    } else {
+      L = idx == 0 ? work_item(bid, nwg, p) : -1;
+      if (L < 0) return it;                  // padding of the last XCD round
+    }
+    int d = rdiv(L, 0);
+    const int g = L - d * group;
+    L = d;
+    d = rdiv(L, 1);
+    const int t = L - d * nqt;
+    L = d;
+    const int b = rdiv(L, 2);
+    const int kvh = L - b * hkv;
+    const int hq = kvh * group + g;
+    const int qt = CAUSAL ? nqt - 1 - t : t;
+    const SeqView sv = seq_view(p, b, hq, kvh);
+    it.q0 = qt * BRW;
+    if (it.q0 >= sv.nq) return it;           // a packed sequence shorter than the longest
+    it.q = sv.q; it.k = sv.k; it.v = sv.v; it.o = sv.o; it.lse = sv.lse;
+    it.nq = sv.nq; it.nk = sv.nk;
+    const int kv_end = CAUSAL ? min(it.nk, it.q0 + BRW) : it.nk;
+    // tiles wholly behind every row's window are never loaded
+    it.jbase = (CAUSAL && p.window >= 0) ? max(0, it.q0 - p.window) / BC : 0;
+    it.ntiles = (kv_end + BC - 1) / BC - it.jbase;
+    it.valid = true;
+    return it;
+  };
+  int idx = 0;
+  const Item it0 = make_item(0);
+  if (!it0.valid) return;                    // whole workgroup
+  // the current item (its first K/V tile is stream tile c_t0)
+  int c_t0 = 0, c_nt = it0.ntiles, c_nk = it0.nk, c_jb = it0.jbase, c_q0 = it0.q0, c_nq = it0.nq;
+  int64_t c_o = it0.o, c_lse = it0.lse;
 
-  const SeqView sv = seq_view(p, b, hq, kvh);
-  const int q0 = qt * BRW;
-  const int nq = sv.nq, nk = sv.nk;
-  if (q0 >= nq) return;                      // a packed sequence shorter than the longest (whole workgroup)
-  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(p.q) + sv.q;
-  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(p.k) + sv.k;
-  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(p.v) + sv.v;
-  const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2];
-
-  const int wrow0 = q0 + wave * 32;
-  const int row = wrow0 + r32;
+  const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q);
+  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k);
+  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v);
+  const int64_t ks2 = p.k_stride[2], vs2 = p.v_stride[2], qs2 = p.q_stride[2];
   const int W = CAUSAL ? p.window : -1;      // sliding window (row r sees keys r-W .. r)
-  const int kv_end = CAUSAL ? min(nk, q0 + BRW) : nk;
-  // Tile indices below count from the workgroup's first needed tile jbase
-  // (tiles wholly behind every row's window are never loaded).
-  const int jbase = W >= 0 ? max(0, q0 - W) / BC : 0;
-  const int ntiles = (kv_end + BC - 1) / BC - jbase;
-  // Tiles this wave needs: [lo_w, nt_w). Without the mask that is every
-  // tile, but the bound is still written in terms of the wave's rows (equal
-  // to ntiles since wrow0 >= 0): a wave-uniform bound lets the compiler turn
-  // the unit loop into uniform branches whose register allocation spills.
-  const int nt_w = CAUSAL ? min(ntiles, (wrow0 + 31) / BC + 1 - jbase) : min(ntiles, (wrow0 + nk + BC - 1) / BC);
-  const int lo_w = W >= 0 ? max(0, wrow0 - W) / BC - jbase : 0;
 
   // DMA plan: this lane's 16-byte chunk of each 1-KB write, as a byte offset
   // inside one key tile, so a load is a scalar tile base plus a 32-bit offset
@@ -604,47 +652,99 @@ void fwd_pp_kernel(const FwdParams p) {
     kofs[i] = (uint32_t)(2 * (r * ks2 + dma_k[i]));
     vofs[i] = (uint32_t)(2 * (r * vs2 + dma_v[i]));
   }
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int tile, int ST) {
-    const int kv0 = (jbase + tile) * BC;
-    const char* kb = reinterpret_cast<const char*>(kp + (int64_t)kv0 * ks2);
-    const char* vb = reinterpret_cast<const char*>(vp + (int64_t)kv0 * vs2);
-    __bf16* dst = smem + ST * 2 * TILE + wave_u * LPW * 512;
-    if (kv0 + BC <= nk) {
+  // this wave's 32 query rows of an item, from row qb on (nr rows are left
+  // before the sequence end; later ones repeat the last), into its part of
+  // the query area
+  auto issue_q = [&](const __bf16* qb, int nr) __attribute__((always_inline)) {
+    __bf16* dst = qsm + wave_u * 32 * D;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));             // keeps the per-lane offsets out of the loops around (registers)
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(kb + kofs[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + vofs[i]), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
-      }
-    } else {                                   // ragged last tile: rows past the end repeat the last row
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int r = min(dma_row[i], nk - 1 - kv0);
-        const uint32_t ko = (uint32_t)(2 * (r * ks2 + dma_k[i])), vo = (uint32_t)(2 * (r * vs2 + dma_v[i]));
-        __builtin_amdgcn_global_load_lds((const void*)(kb + ko), (lds_void*)(dst + i * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + vo), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
-      }
+    for (int i = 0; i < QLPW; ++i) {
+      const int rl = 4 * i + (ln >> 4);
+      const int r = min(rl, nr - 1);
+      const int ch = (ln & 15) ^ (rl & 15);
+      __builtin_amdgcn_global_load_lds((const void*)(qb + (int64_t)r * qs2 + 8 * ch), (lds_void*)(dst + i * 512),
+                                       16, 0, 0);
     }
   };
-  // wait until at most `ahead` tiles of this wave's loads are still in flight
-  auto wait_tiles = [&](int ahead) {
-    if (ahead <= 0) wait_vmcnt<0>();
-    else if (ahead == 1) wait_vmcnt<2 * LPW>();
-    else wait_vmcnt<4 * LPW>();
+
+  // The issue cursor walks the stream: it points at the next K/V tile to
+  // issue (ik, iv; irem keys left in its item from there on) and stops at
+  // the end of the item after the current one (the query area holds one
+  // item's rows ahead).
+  int issued = 0;                            // stream tiles this wave has issued
+  int iend = c_nt;                           // stream index where the cursor's item ends
+  int ilim = 0;                              // and where it has to stop (set with the next item)
+  const char* ik = reinterpret_cast<const char*>(kg + it0.k + (int64_t)it0.jbase * BC * ks2);
+  const char* iv = reinterpret_cast<const char*>(vg + it0.v + (int64_t)it0.jbase * BC * vs2);
+  int irem = it0.nk - it0.jbase * BC;
+  issue_q(qg + it0.q + (int64_t)(it0.q0 + 32 * wave_u) * qs2, it0.nq - it0.q0 - 32 * wave_u);
+  // the next item (read once per item: these may live in spill lanes)
+  Item nx;
+  const char* nx_k;
+  const char* nx_v;
+  const __bf16* nx_q;
+  int nx_nt, nx_rem, nx_qr;
+
+  // Issue the next stream tile (stage ist = issued % STAGES); the first tile
+  // of the next item takes that item's query rows with it.
+  int ist = 0;
+  auto issue_one = [&]() __attribute__((always_inline)) {
+    if (issued == iend) {                    // on into the next item
+      ik = nx_k;
+      iv = nx_v;
+      irem = nx_rem;
+      iend += nx_nt;
+      issue_q(nx_q, nx_qr);
+    }
+    __bf16* dst = smem + ist * 2 * TILE + wave_u * LPW * 512;
+    if (irem >= BC) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(ik + kofs[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(iv + vofs[i]), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
+      }
+    } else {                                 // ragged last tile: rows past the end repeat the last row
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = min(dma_row[i], irem - 1);
+        const uint32_t ko = (uint32_t)(2 * (r * ks2 + dma_k[i])), vo = (uint32_t)(2 * (r * vs2 + dma_v[i]));
+        __builtin_amdgcn_global_load_lds((const void*)(ik + ko), (lds_void*)(dst + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(iv + vo), (lds_void*)(dst + TILE + i * 512), 16, 0, 0);
+      }
+    }
+    ik += 2 * BC * ks2;
+    iv += 2 * BC * vs2;
+    irem -= BC;
+    ++issued;
+    ist = ist == STAGES - 1 ? 0 : ist + 1;
+  };
+  // issue the stream up to tile `last`, within the current and the next item
+  auto issue_upto = [&](int last) __attribute__((always_inline)) {
+    const int lim = min(last + 1, ilim);
+    while (issued < lim) issue_one();
+  };
+  // wait until this wave's loads of stream tile g of the current item (and
+  // everything older) have landed: the loads younger than g are the later
+  // tiles issued so far, plus the next item's query rows once the cursor has
+  // moved into that item
+  auto wait_for = [&](int g) __attribute__((always_inline)) {
+    const int y = 2 * LPW * (issued - g - 1) + (issued > c_t0 + c_nt ? QLPW : 0);
+    if (y >= 2 * LPW * 3 + QLPW) wait_vmcnt<2 * LPW * 3 + QLPW>();
+    else if (y >= 2 * LPW * 2 + QLPW) wait_vmcnt<2 * LPW * 2 + QLPW>();
+    else if (y >= 2 * LPW + QLPW) wait_vmcnt<2 * LPW + QLPW>();
+    else if (y >= 2 * LPW * 2) wait_vmcnt<2 * LPW * 2>();
+    else if (y >= 2 * LPW) wait_vmcnt<2 * LPW>();
+    else wait_vmcnt<0>();
   };
   // workgroup barrier without the fence of __syncthreads (which would also
   // drain the loads still in flight for later tiles)
-  auto barrier = [&]() {
+  auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-
-  bf16x8 qf[KSTEPS];
-#pragma unroll
-  for (int kc = 0; kc < KSTEPS; ++kc)
-    qf[kc] = as_bf16x8(row < nq ? load16(qp + (int64_t)row * p.q_stride[2] + 16 * kc + 8 * half)
-                                : u32x4{0, 0, 0, 0});
 
   int koff[KSTEPS];
   {
@@ -662,30 +762,30 @@ void fwd_pp_kernel(const FwdParams p) {
       voff[db] = r * D + 8 * ((col >> 3) ^ vswz_t<D>(r)) + (col & 7);
     }
   }
-
-  const float c2 = p.scale_log2;
-  float m_run = kNegInf, l_run = 0.f;
-  float m_use = 0.f;                    // m_run, or 0 while no key has been seen
   // Sum of the bf16 weights that enter P V, on the matrix core (v_dot2c runs
   // on the matrix pipe too, so it would stall the other group's MFMAs): a
   // P^T chunk read as the B operand of v_mfma_f32_16x16x32_bf16 holds, in
   // column n, keys 0-7 and 8-15 of rows n and n+16; the A operand below is 1
   // where the key group belongs to the row this lane's accumulator holds
   // (row lane % 32), so every register of lsum is that row's running sum.
-  f32x4 lsum = f32x4{};
   bf16x8 lsel;
   {
     const __bf16 one = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.f : (__bf16)0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) lsel[e] = one;
   }
+
+  const float c2 = p.scale_log2;
+  bf16x8 qf[KSTEPS];
+  float m_run, l_run, m_use;                 // m_use: m_run, or 0 while no key has been seen
+  f32x4 lsum;
   f32x16 o[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
   f32x16 sc[2];          // scores of the tile the next S unit works on
   bf16x8 pb[4];          // P^T of the tile the next G unit accumulates
+  // per-item geometry of this wave
+  int wrow0, row, nt_w, lo_w;
 
-  auto scores = [&](int ST) {
+  auto scores = [&](int ST) __attribute__((always_inline)) {
     const __bf16* ks = smem + ST * 2 * TILE;
     sc[0] = sc[1] = f32x16{};
 #pragma unroll
@@ -696,7 +796,7 @@ void fwd_pp_kernel(const FwdParams p) {
       sc[1] = mfma32(k1, qf[kc], sc[1]);
     }
   };
-  auto accumulate = [&](int ST) {
+  auto accumulate = [&](int ST) __attribute__((always_inline)) {
     const __bf16* vs = smem + ST * 2 * TILE + TILE;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -716,23 +816,24 @@ void fwd_pp_kernel(const FwdParams p) {
   // before the MFMA that consumes them (a scheduling barrier after each step
   // keeps that order): K for the 8 score k-steps, then V (two transposing
   // reads per PV MFMA) for the 16 PV MFMAs.
-  auto gunit = [&](int SK, int SV) {
+  auto gunit = [&](int SK, int SV) __attribute__((always_inline)) {
     constexpr int AHEAD = FA_FWD_AHEAD;
     const __bf16* ks = smem + SK * 2 * TILE;
     const __bf16* vs = smem + SV * 2 * TILE + TILE;
     bf16x8 kf[KSTEPS][2];
     bf16x4 vf[4 * DBLK][2];
-    auto read_k = [&](int kc) {
+    auto read_k = [&](int kc) __attribute__((always_inline)) {
       kf[kc][0] = *reinterpret_cast<const bf16x8*>(ks + koff[kc]);
       kf[kc][1] = *reinterpret_cast<const bf16x8*>(ks + 32 * D + koff[kc]);
     };
-    auto read_v = [&](int i) {                 // PV step i: key chunk i / DBLK, d block i % DBLK
+    // PV step i: key chunk i / DBLK, d block i % DBLK
+    auto read_v = [&](int i) __attribute__((always_inline)) {
       const __bf16* va = vs + voff[i % DBLK] + 16 * (i / DBLK) * D;
       vf[i][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
       vf[i][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
     };
     // reads in consumption order: K k-steps 0..KSTEPS-1, then V steps 0..4*DBLK-1
-    auto read = [&](int x) {
+    auto read = [&](int x) __attribute__((always_inline)) {
       if (x < KSTEPS) read_k(x);
       else if (x < KSTEPS + 4 * DBLK) read_v(x - KSTEPS);
     };
@@ -757,7 +858,8 @@ void fwd_pp_kernel(const FwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto softmax = [&](int kv0) {
+  auto softmax = [&](int kv0) __attribute__((always_inline)) {
+    const int nk = c_nk;
     const bool win = W >= 0 && kv0 < wrow0 + 31 - W;
     if ((CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > nk) || win) {
       const int kmin = win ? row - W : -1;
@@ -806,63 +908,99 @@ void fwd_pp_kernel(const FwdParams p) {
     l_run += half_swap_sum(rs);
   };
 
-  // phase bookkeeping shared by every wave: at the start of phase 2t+4 the
-  // stage of tile t is refilled with tile t+STAGES; before the barrier that
+  // Phases are numbered within the current item: at phase 2t+4 (group 1) or
+  // 2t+5 (group 0) a wave issues its share of stream tile g+STAGES into the
+  // stage of the item's tile t (stream tile g); before the barrier that
   // opens phase 2t, tile t must have landed.
-  const int nunits = 2 * ntiles + 1;              // G(-1), S(0), G(0), ..., S(nt-1), G(nt-1)
-  const int nph = nunits + 1;
-  auto phase_begin = [&](int ph) {
-#if FA_FWD_DMA_SPLIT
-    // each wave issues its share of tile tt + STAGES in its own softmax
-    // phase, off the matrix-core units: group 1 at phase 2tt+4, group 0 one
-    // phase later. At every odd phase's end both groups have issued the same
-    // tiles, so the waits below are unchanged.
-    const int pg = ph - 4 - (grp == 0 ? 1 : 0);
-    if (pg >= 0 && !(pg & 1)) {
-      const int tt = pg >> 1;
-      if (tt + STAGES < ntiles) issue(tt + STAGES, tt % STAGES);
+  //   After an item's start, where the stream stands at least STAGES tiles
+  // into the item (or at the end of the next one), each such step frees one
+  // stage and the stream moves on by at most one tile. When tile t >= 2 is
+  // waited for (end of phase 2t-1), the last step taken was that of tile
+  // t-3, so no later tile is in flight: everything this wave has issued must
+  // land. Tiles 0 and 1 are waited for at the item's start.
+  // ev_ph: this wave's next refill phase; permit: the last stream tile whose
+  // stage is free by then
+  int ev_ph, permit;
+  auto phase_begin = [&](int ph) __attribute__((always_inline)) {
+    if (ph == ev_ph) {
+      ev_ph += 2;
+      ++permit;
+      if (issued <= permit && issued < ilim) issue_one();
     }
-#else
-    if (ph >= 4 && !(ph & 1)) {
-      const int tt = (ph - 4) >> 1;
-      if (tt + STAGES < ntiles) issue(tt + STAGES, tt % STAGES);
-    }
-#endif
   };
-  auto phase_end = [&](int ph) {
+  auto phase_end = [&](int ph, int nph) __attribute__((always_inline)) {
     if (ph + 1 >= nph) return;
-    if (ph & 1) {
-      const int tt = (ph + 1) >> 1;
-      if (tt < ntiles) wait_tiles(min(ntiles - 1, max(STAGES - 1, tt + STAGES - 3)) - tt);
-    }
+    // tile (ph + 1) / 2 is read from the next phase on
+    if ((ph & 1) && ph >= 3 && ph < 2 * c_nt - 1) wait_vmcnt<0>();
     barrier();
   };
 
-#pragma unroll
-  for (int i = 0; i < STAGES; ++i)
-    if (i < ntiles) issue(i, i);
-  wait_tiles(min(STAGES, ntiles) - 1);
-  barrier();
+  for (;;) {
+    nx = make_item(idx + 1);
+    nx_nt = nx.valid ? nx.ntiles : 0;
+    ilim = iend + nx_nt;
+    nx_k = reinterpret_cast<const char*>(kg + nx.k + (int64_t)nx.jbase * BC * ks2);
+    nx_v = reinterpret_cast<const char*>(vg + nx.v + (int64_t)nx.jbase * BC * vs2);
+    nx_rem = nx.nk - nx.jbase * BC;
+    nx_q = qg + nx.q + (int64_t)(nx.q0 + 32 * wave_u) * qs2;
+    nx_qr = nx.nq - nx.q0 - 32 * wave_u;
 
-  if (grp == 1) {                                   // group 1 idles through phase 0
-    phase_begin(0);
-    phase_end(0);
-  }
-  // units u = 0 .. 2 ntiles, unrolled over 2 STAGES units so stages are constants
-  for (int u0 = 0; u0 < nunits; u0 += 2 * STAGES) {
+    // Item start: its first tiles (and query rows) are issued, mostly during
+    // the previous item already. The query rows are read before the stream
+    // may run on into the next item, whose rows take their place.
+    issue_upto(min(c_t0 + STAGES, c_t0 + c_nt) - 1);
+    wait_for(c_t0 + min(1, c_nt - 1));
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));           // addresses made here, not kept from before the item loop
+      const __bf16* qr = qsm + wave_u * 32 * D + (ln & 31) * D;
+      const int c0 = (ln >> 5) ^ (ln & 15);
 #pragma unroll
-    for (int r = 0; r < 2 * STAGES; ++r) {
-      const int u = u0 + r;
-      if (u >= nunits) break;
+      for (int kc = 0; kc < KSTEPS; ++kc)
+        qf[kc] = *reinterpret_cast<const bf16x8*>(qr + 8 * (c0 ^ (2 * kc)));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    issue_upto(c_t0 + STAGES - 1);
+    barrier();
+
+    wrow0 = c_q0 + wave * 32;
+    row = wrow0 + r32;
+    // Tiles this wave needs: [lo_w, nt_w). Without the mask that is every
+    // tile, but the bound is still written in terms of the wave's rows (equal
+    // to ntiles since wrow0 >= 0): a wave-uniform bound lets the compiler turn
+    // the unit loop into uniform branches whose register allocation spills.
+    nt_w = CAUSAL ? min(c_nt, (wrow0 + 31) / BC + 1 - c_jb)
+                  : min(c_nt, (wrow0 + c_nk + BC - 1) / BC);
+    lo_w = W >= 0 ? max(0, wrow0 - W) / BC - c_jb : 0;
+    m_run = kNegInf;
+    l_run = 0.f;
+    m_use = 0.f;
+    lsum = f32x4{};
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+
+    const int nunits = 2 * c_nt + 1;   // G(-1), S(0), G(0), ..., S(nt-1), G(nt-1)
+    const int nph = nunits + 1;
+    ev_ph = grp == 0 ? 5 : 4;
+    permit = c_t0 + STAGES - 1;
+    if (grp == 1) {                          // group 1 idles through phase 0
+      phase_begin(0);
+      phase_end(0, nph);
+    }
+    // Unit u (r = its position in a round of 2 STAGES units; the stages it
+    // reads are constants of r). Returns false past the last unit.
+    auto unit = [&](int u, auto rc) __attribute__((always_inline)) -> bool {
+      constexpr int r = decltype(rc)::value;
+      if (u >= nunits) return false;
       const int ph = u + grp;
       phase_begin(ph);
-      if (r & 1) {                                  // S(j), j = (u - 1) / 2
+      if constexpr (r & 1) {                          // S(j), j = (u - 1) / 2
         const int j = (u - 1) >> 1;
-        if (j >= lo_w && j < nt_w) softmax((jbase + j) * BC);
-      } else {                                      // G(j), j = u / 2 - 1
+        if (j >= lo_w && j < nt_w) softmax((c_jb + j) * BC);
+      } else {                                        // G(j), j = u / 2 - 1
         const int j = (u >> 1) - 1;
-        const int SK = (r / 2) % STAGES;            // stage of tile j + 1 (a constant once unrolled)
-        const int SV = (r / 2 + STAGES - 1) % STAGES;       // stage of tile j
+        constexpr int SK = (r / 2) % STAGES;          // stage of tile j + 1
+        constexpr int SV = (r / 2 + STAGES - 1) % STAGES;     // stage of tile j
 #if FA_FWD_PRIO
         __builtin_amdgcn_s_setprio(1);
 #endif
@@ -875,34 +1013,63 @@ void fwd_pp_kernel(const FwdParams p) {
         __builtin_amdgcn_s_setprio(0);
 #endif
       }
-      phase_end(ph);
+      phase_end(ph, nph);
+      return true;
+    };
+    // The item's tile t is stream tile c_t0 + t, in stage (c_t0 + t) % 3, so
+    // its units start at position 2 (c_t0 % 3) of a round: the partial first
+    // round is peeled off.
+    const int rot = c_t0 % STAGES;
+    int ub = 0;
+    bool more = true;
+    if (rot == 1) {
+      more = unit(0, int_c<2>{}) && unit(1, int_c<3>{});
+      ub = 2;
     }
-  }
-  if (grp == 0) phase_begin(nph - 1);              // group 0 idles through the last phase
-
-  if (row < nq) {
-    const float l_o = lsum[0];
-    const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
-    TOut* op = reinterpret_cast<TOut*>(p.o) + sv.o + (int64_t)row * p.o_stride[2];
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * half;
-        const float v0 = o[db][4 * gq + 0] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
-        const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
-        if constexpr (sizeof(TOut) == 4) {
-          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
-        } else {
-          bf16x4 h;
-          h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
-          *reinterpret_cast<bf16x4*>(op + d) = h;
-        }
+    if (more && rot != 0) {
+      more = unit(ub, int_c<4>{}) && unit(ub + 1, int_c<5>{});
+      ub += 2;
+    }
+    if (more) {
+      for (;; ub += 6) {
+        if (!unit(ub + 0, int_c<0>{}) || !unit(ub + 1, int_c<1>{}) || !unit(ub + 2, int_c<2>{}) ||
+            !unit(ub + 3, int_c<3>{}) || !unit(ub + 4, int_c<4>{}) || !unit(ub + 5, int_c<5>{}))
+          break;
       }
-    if (p.lse != nullptr && half == 0) {
-      const float lse = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
-      p.lse[sv.lse + row] = lse;
     }
+    if (grp == 0) phase_begin(nph - 1);              // group 0 idles through the last phase
+
+    if (row < c_nq) {
+      const float l_o = lsum[0];
+      const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
+      TOut* op = reinterpret_cast<TOut*>(p.o) + c_o + (int64_t)row * p.o_stride[2];
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * half;
+          const float v0 = o[db][4 * gq + 0] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
+          const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
+          if constexpr (sizeof(TOut) == 4) {
+            *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+          } else {
+            bf16x4 h;
+            h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
+            *reinterpret_cast<bf16x4*>(op + d) = h;
+          }
+        }
+      if (p.lse != nullptr && half == 0) {
+        const float lse = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+        p.lse[c_lse + row] = lse;
+      }
+    }
+    if (nx_nt == 0) break;                            // no next item
+    barrier();                                        // the last phase's reads end before its stage is refilled
+    issue_upto(c_t0 + c_nt);                          // the next item's first tile (normally issued already)
+    ++idx;
+    c_t0 += c_nt;
+    c_nt = nx.ntiles; c_nk = nx.nk; c_jb = nx.jbase; c_q0 = nx.q0; c_nq = nx.nq;
+    c_o = nx.o; c_lse = nx.lse;
   }
 }
 
@@ -923,12 +1090,32 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (the persistent grid's size).
+inline int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, bool CAUSAL, typename TOut, int STAGES>
 hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
   q.n_qtiles = (p.seqlen_q + 255) / 256;
   q.n_items = q.batch * q.heads_q * q.n_qtiles;
-  const int64_t wgs = grid_for(q);
+  fa_reciprocal(q.group, &q.div_m[0], &q.div_s[0]);
+  fa_reciprocal(q.n_qtiles, &q.div_m[1], &q.div_s[1]);
+  fa_reciprocal(q.heads_kv, &q.div_m[2], &q.div_s[2]);
+  // dense: one workgroup per compute unit (one fits, by its LDS), a whole
+  // number per XCD; packed: one per work item
+  const int64_t wgs = q.cu_seqlens != nullptr
+                          ? grid_for(q)
+                          : std::min<int64_t>(std::max(8, device_cus() / 8 * 8), ((int64_t)q.n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((detail::fwd_pp_kernel<D, CAUSAL, TOut, STAGES>), dim3((unsigned)wgs), dim3(512), 0, stream, q);
   return hipGetLastError();
 }

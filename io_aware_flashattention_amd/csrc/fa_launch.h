@@ -26,7 +26,23 @@ struct FwdParams {
   const int32_t* cu_seqlens;
   int total;
   int window;        // sliding window (causal only): row r sees keys r-window .. r; -1 for none
+  // Reciprocals of group, n_qtiles and heads_kv for the work-item decode
+  // (filled in by the launchers): n / d = umulhi(n, m) >> (s - 1) for
+  // 0 <= n < 2^31, with s = ceil(log2 d) and m = ceil(2^(31+s) / d); m = 0
+  // stands for d = 1.
+  uint32_t div_m[3];
+  int div_s[3];
 };
+
+// The reciprocal (m, s) of d >= 1 described at FwdParams::div_m. With
+// e = m d - 2^(31+s) < d <= 2^s, n m / 2^(31+s) exceeds n / d by less than
+// n 2^-(31+s) < 2^-s <= 1/d, which never reaches the next integer.
+inline void fa_reciprocal(int d, uint32_t* m, int* s) {
+  int k = 0;
+  while ((1LL << k) < d) ++k;
+  *s = k;
+  *m = d == 1 ? 0u : (uint32_t)((((uint64_t)1 << (31 + k)) + (uint64_t)d - 1) / (uint64_t)d);
+}
 
 struct DecodeParams {
   const void* q;       // [B, Hq, d] bf16
