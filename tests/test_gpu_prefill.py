@@ -133,6 +133,22 @@ def test_c4_long_context_gqa(name):
     run_and_check(q, k, v, cfg.causal, cfg.scale, name, rows=rows)
 
 
+@pytest.mark.parametrize("B,causal", [(2, True), (3, False)])
+def test_persistent_items_with_ragged_tiles(B, causal):
+    """More work items than workgroups, so every workgroup of the persistent
+    grid takes two or three, with a ragged last key tile: B x Hq64 Hkv8
+    N1000 d128 (4 query tiles per head; 512 or 768 items). K/V tiles and query
+    rows then stream across item boundaries, and items start in every stage
+    of the ring (16 key tiles per non-causal item; 4..16 under the mask).
+    Sampled rows of every head: first and last, tile edges, and one more."""
+    q, k, v = W.make_random_prefill(B, 64, 8, 1000, 1000, 128, seed=4242 + B, heavy_frac=0.01)
+    base = [0, 1, 63, 64, 255, 256, 257, 511, 512, 767, 768, 960, 998, 999]
+
+    def rows(b, h):
+        return np.array(sorted(set(base) | {(37 * h + 11 * b) % 1000}))
+    run_and_check(q, k, v, causal, 1 / np.sqrt(128), f"persistent B{B} N1000 causal={causal}", rows=rows)
+
+
 def test_gqa_bit_identical_to_replicated_kv():
     q, k, v = W.make_random_prefill(2, 8, 2, 300, 300, 128, seed=5, heavy_frac=0.01)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
