@@ -513,7 +513,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 // the matrix core while the other runs the softmax, and the two swap at the
 // next barrier.
 //
-// A dense batch runs on a persistent grid: one workgroup per compute unit,
+// A dense batch (or a packed batch of one sequence) runs on a persistent
+// grid: one workgroup per compute unit,
 // each with a fixed list of work items, and the K/V tiles of a workgroup's
 // consecutive items form one stream through the ring. Stream tile g sits in
 // stage g % STAGES; within its item (index t there) it is read in phases
@@ -566,15 +567,31 @@ void fwd_pp_kernel(const FwdParams p) {
     __syncthreads();
   }
 
-  // Work items of this workgroup. Dense: the workgroups of XCD x (blockIdx % 8,
+  // Work items of this workgroup. Persistent grid (a dense batch, or a packed
+  // batch of one sequence, whose items cost what a dense batch's do): the
+  // workgroups of XCD x (blockIdx % 8,
   // the dispatcher's round-robin) share the contiguous range of the logical
   // order that work_item gives x, dealt out in a snake (round k left to right
   // for even k, right to left for odd k). Each (batch, kv head) row of the
   // logical order lists its query tiles heaviest first, with the query heads
   // of a kv head side by side, so two consecutive rounds give the workgroups
   // nearly the same causal cost (the same when a row holds whole pairs of
-  // rounds and a round whole groups of heads).
-  const bool dense = p.cu_seqlens == nullptr;
+  // rounds and a round whole groups of heads). A packed sequence's real
+  // length (the caller's longest length may overstate it) sets its item count
+  // and query-tile count here, with that count's reciprocal.
+  const bool persist = p.persist;
+  int n_items = p.n_items, n_qt = p.n_qtiles;
+  uint32_t qt_m = p.div_m[1];
+  int qt_s = p.div_s[1];
+  if (persist && p.cu_seqlens != nullptr) {
+    const const_i32* cu = (const const_i32*)p.cu_seqlens;
+    const int s0 = min(max(cu[0], 0), p.total);
+    const int s1 = min(max(cu[1], s0), p.total);
+    n_qt = (s1 - s0 + BRW - 1) / BRW;
+    n_items = p.heads_q * n_qt;
+    qt_s = n_qt <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n_qt - 1));
+    qt_m = n_qt <= 1 ? 0u : (uint32_t)((((uint64_t)1 << (31 + qt_s)) + (uint64_t)n_qt - 1) / (uint64_t)n_qt);
+  }
   struct Item {
     int64_t q, k, v, o, lse;                 // element offsets of its (sequence, head)
     int nq, nk, q0, jbase, ntiles;
@@ -585,15 +602,16 @@ void fwd_pp_kernel(const FwdParams p) {
   // live in registers through them; the divisions are multiply-shifts by the
   // launcher's reciprocals)
   auto rdiv = [&](int n, int which) __attribute__((always_inline)) {
-    const uint32_t m = p.div_m[which];
-    return m == 0 ? n : (int)(__umulhi((uint32_t)n, m) >> (p.div_s[which] - 1));
+    const uint32_t m = which == 1 ? qt_m : p.div_m[which];
+    const int sh = which == 1 ? qt_s : p.div_s[which];
+    return m == 0 ? n : (int)(__umulhi((uint32_t)n, m) >> (sh - 1));
   };
   auto make_item = [&](int idx) __attribute__((always_inline)) {
     Item it{};
-    int n = p.n_items, bid = blockIdx.x, nwg = gridDim.x, group = p.group, nqt = p.n_qtiles, hkv = p.heads_kv;
+    int n = n_items, bid = blockIdx.x, nwg = gridDim.x, group = p.group, nqt = n_qt, hkv = p.heads_kv;
     asm volatile("" : "+s"(n), "+s"(bid), "+s"(nwg), "+s"(group), "+s"(nqt), "+s"(hkv), "+s"(idx));
     int L;
-    if (dense) {
+    if (persist) {
       const int per = n >> 3, rem = n & 7, x = bid & 7;
       const int nslot = nwg >> 3, slot = bid >> 3;
       const int pos = idx * nslot + ((idx & 1) ? nslot - 1 - slot : slot);
@@ -1111,9 +1129,11 @@ hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   fa_reciprocal(q.group, &q.div_m[0], &q.div_s[0]);
   fa_reciprocal(q.n_qtiles, &q.div_m[1], &q.div_s[1]);
   fa_reciprocal(q.heads_kv, &q.div_m[2], &q.div_s[2]);
-  // dense: one workgroup per compute unit (one fits, by its LDS), a whole
-  // number per XCD; packed: one per work item
-  const int64_t wgs = q.cu_seqlens != nullptr
+  // persistent (dense, or packed with one sequence): one workgroup per
+  // compute unit (one fits, by its LDS), a whole number per XCD; packed: one
+  // per work item
+  q.persist = q.cu_seqlens == nullptr || q.batch == 1;
+  const int64_t wgs = !q.persist
                           ? grid_for(q)
                           : std::min<int64_t>(std::max(8, device_cus() / 8 * 8), ((int64_t)q.n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((detail::fwd_pp_kernel<D, CAUSAL, TOut, STAGES>), dim3((unsigned)wgs), dim3(512), 0, stream, q);

@@ -32,6 +32,7 @@ struct FwdParams {
   // stands for d = 1.
   uint32_t div_m[3];
   int div_s[3];
+  bool persist;      // d = 128 kernel: a persistent grid walks the items (set by its launcher)
 };
 
 // The reciprocal (m, s) of d >= 1 described at FwdParams::div_m. With

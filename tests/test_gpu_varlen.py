@@ -95,6 +95,23 @@ def test_window_8k():
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("causal,window", [(True, None), (False, None), (True, 200)])
+def test_one_sequence_with_overstated_max_len(causal, window):
+    """A packed batch of one sequence runs on the persistent grid. The
+    caller's longest length (1500) overstates the sequence (700), so half the
+    query-tile positions (6 per head, 3 real) lie past its end and are
+    skipped, the heavy causal ones first. Hq64 Hkv8 d128: 384 positions on
+    256 workgroups. Every 7th row of every head, and the tile edges."""
+    lens = np.array([700])
+    q, k, v, cu = W.make_varlen_inputs(64, 8, 128, lens, seed=777)
+    say(f"case one sequence of 700 (max_len 1500) causal={causal} window={window}")
+    o, lse = _run(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(cu).to("cuda"), 1500, causal, window)
+    rows = sorted(set(range(0, 700, 7)) | {255, 256, 511, 512, 699})
+    o_ref, l_ref = varlen_ref(q, k, v, cu, 1.0 / np.sqrt(128), causal=causal, window=window, rows=rows,
+                              values=W.to_f64)
+    check(o[rows], lse[:, rows], o_ref[rows], l_ref[:, rows], f"one sequence causal={causal} window={window}")
+
+
 def test_varlen_mixed_lengths_gqa():
     cfg = W.VARLEN_CONFIGS["c6_varlen_causal"]
     lens = W.varlen_lengths(cfg)
