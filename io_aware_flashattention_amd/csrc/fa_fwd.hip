@@ -514,8 +514,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 // next barrier.
 //
 // A dense batch (or a packed batch of one sequence) runs on a persistent
-// grid: one workgroup per compute unit,
-// each with a fixed list of work items, and the K/V tiles of a workgroup's
+// grid: one workgroup per compute unit, each with a fixed list of work
+// items, and the K/V tiles of a workgroup's
 // consecutive items form one stream through the ring. Stream tile g sits in
 // stage g % STAGES; within its item (index t there) it is read in phases
 // 2t .. 2t+3, and its stage is refilled with stream tile g+STAGES at phase
@@ -523,8 +523,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 // fills with the next item's first tiles. The next item's query rows go
 // global -> LDS together with its first tile: an item starts with its Q and
 // its first K/V tiles on chip, and no workgroup launch separates two items.
-// A packed batch keeps one item per workgroup and leaves the balancing of its
-// mixed lengths to the hardware dispatcher.
+// A packed batch of several sequences keeps one item per workgroup and leaves
+// the balancing of its mixed lengths to the hardware dispatcher.
 template <int D, bool CAUSAL, typename TOut, int STAGES>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const FwdParams p) {
