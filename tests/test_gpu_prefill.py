@@ -149,6 +149,26 @@ def test_persistent_items_with_ragged_tiles(B, causal):
     run_and_check(q, k, v, causal, 1 / np.sqrt(128), f"persistent B{B} N1000 causal={causal}", rows=rows)
 
 
+# (B, Hq, Hkv, N, causal): 1 to 4 items per workgroup of the persistent grid,
+# kv groups of 1, 2 and 8, ragged and whole last key tiles
+SWEEP = [(1, 128, 128, 700, True), (2, 96, 48, 517, False), (4, 64, 8, 384, True), (1, 256, 32, 1100, True),
+         (3, 40, 5, 830, False), (2, 160, 20, 960, True)]
+
+
+@pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n"))
+def test_persistent_shape_sweep(shape):
+    """Seeded shapes whose item counts give the persistent workgroups one to
+    four items each; sampled rows of every head (edges, tile boundaries and a
+    head-dependent row)."""
+    B, Hq, Hkv, N, causal = shape
+    q, k, v = W.make_random_prefill(B, Hq, Hkv, N, N, 128, seed=900 + N, heavy_frac=0.02)
+    edges = [0, 1, 63, 64, 255, 256, N // 2, N - 65, N - 64, N - 2, N - 1]
+
+    def rows(b, h):
+        return np.array(sorted({r for r in edges if 0 <= r < N} | {(53 * h + 17 * b) % N}))
+    run_and_check(q, k, v, causal, 1 / np.sqrt(128), f"sweep B{B} Hq{Hq} Hkv{Hkv} N{N} causal={causal}", rows=rows)
+
+
 def test_gqa_bit_identical_to_replicated_kv():
     q, k, v = W.make_random_prefill(2, 8, 2, 300, 300, 128, seed=5, heavy_frac=0.01)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
