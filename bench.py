@@ -98,7 +98,7 @@ def run(args):
     lens_d = torch.from_numpy(lens).to(dev)
     do = torch.empty(dc.batch, dc.heads_q, dc.head_dim, dtype=torch.bfloat16, device=dev)
     dlse = torch.empty(dc.batch, dc.heads_q, dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.decode_workspace_bytes(dc.batch, dc.heads_q, dc.heads_kv, dc.max_len, dc.head_dim),
+    ws = torch.empty(fa.decode_workspace_bytes(dc.batch, dc.heads_q, dc.heads_kv, dc.max_len, dc.head_dim, 0),
                      dtype=torch.uint8, device=dev)
     # calibration copy of known size (its FETCH/WRITE counters scale the HBM byte counters)
     csrc = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

@@ -33,8 +33,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
- *     allocates and frees nothing and keeps no state between calls except the
- *     calling thread's last error message.
+ *     allocates and frees nothing. Its only state between calls is the calling
+ *     thread's last error message and a per-device cache of the compute-unit
+ *     count (read once from the runtime, held in atomics).
  *   - Calls are asynchronous: FA_OK means the work was enqueued on `stream`
  *     (a hipStream_t passed as void*, NULL = the default stream). Results are
  *     valid once the caller synchronises that stream. Device faults surface at
@@ -153,13 +154,18 @@ FA_API fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, vo
                           void* stream);
 
 /*
- * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes:
- * float32 partial outputs and log-sum-exps, one set of heads_q/heads_kv heads
- * per piece of work (at most batch*heads_kv plus the decode grid's size).
+ * fa_decode_workspace_bytes -- device workspace fa_decode (and fa_decode_paged)
+ * needs for these sizes and this split_tokens: float32 partial outputs and
+ * log-sum-exps, one set of heads_q/heads_kv heads per piece of work. A piece
+ * is the part of one (sequence, kv head) slab that falls in one workgroup's
+ * range; the ranges cut the slabs at most (grid size - 1) times, so there are
+ * at most batch*heads_kv plus the decode grid's size pieces for any
+ * split_tokens, and the size returned does not change with it (the argument
+ * is kept so a caller sizes the workspace for exactly the call it makes).
  * Returns 0 for invalid sizes.
  */
 FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                        int32_t max_seqlen_k, int32_t head_dim);
+                                        int32_t max_seqlen_k, int32_t head_dim, int32_t split_tokens);
 
 /*
  * fa_decode -- one query token per sequence against a contiguous KV cache.
@@ -179,11 +185,12 @@ FA_API size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t 
  *          as the grid allows. LSE does not depend on it beyond float32
  *          rounding; O may move by the bf16 rounding of the probabilities,
  *          which each range takes relative to its own running maximum.
- * workspace      device buffer of at least fa_decode_workspace_bytes(...) bytes,
+ * workspace      device buffer of at least fa_decode_workspace_bytes(batch,
+ *          heads_q, heads_kv, max_seqlen_k, head_dim, split_tokens) bytes,
  *          16-byte aligned; its contents on entry do not matter and are
  *          overwritten. Two calls that share a workspace must be ordered.
  *
- * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
+ * Supported: head_dim 64 or 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
  * bf16 q and cache; pointers 16-byte aligned; kv strides multiples of 8.
  * Every cache row a sequence may read (index < its length) must lie inside
  * the caches; rows at or past a sequence's length are never read.
@@ -220,9 +227,10 @@ FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_c
  *              a length of 0 yields O = 0 and LSE = -inf
  * o, lse, out_dtype, softmax_scale, split_tokens: as for fa_decode
  * workspace    at least fa_decode_workspace_bytes(batch, heads_q, heads_kv,
- *              max_blocks_per_seq * page_size, head_dim) bytes, 16-byte aligned
+ *              max_blocks_per_seq * page_size, head_dim, split_tokens) bytes,
+ *              16-byte aligned
  *
- * Supported: head_dim 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
+ * Supported: head_dim 64 or 128; heads_q % heads_kv == 0 and heads_q / heads_kv <= 32;
  * page_size >= 16 (a 32-key block then spans at most three pages); pointers
  * 16-byte aligned; page strides multiples of 8 elements; page_size *
  * page_stride[2] < 2^31 elements. Otherwise FA_ERR_UNSUPPORTED.

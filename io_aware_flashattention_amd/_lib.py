@@ -22,7 +22,8 @@ FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd_workspace_bytes", "fa_bwd", "fa_fp8_quantize", "fa_fwd_fp8",
-            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string", "fa_last_error_message")
+            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string",
+            "fa_last_error_message")
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
 _lib = None
@@ -65,7 +66,7 @@ def load():
     lib.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
-    lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]   # batch, heads_q, heads_kv, max_seqlen, head_dim
+    lib.fa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]   # batch, Hq, Hkv, max_seqlen, d, split
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
                               ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
@@ -105,6 +106,40 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _shape(t: torch.Tensor, want: tuple, name: str):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _dims(t: torch.Tensor, n: int, name: str):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _on_gpu(*named):
+    """Every tensor on one GPU (the C ABI takes device pointers and cannot
+    tell a host pointer from a device one, so this is checked here)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU, got device {t.device}")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other operands on {dev}")
+        dev = t.device
+
+
+def _lse_arg(lse, want: tuple, device):
+    if lse is True:
+        return torch.empty(want, dtype=torch.float32, device=device)
+    if lse is False or lse is None:
+        return None
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(want):
+        raise ValueError(f"lse must be a contiguous float32 {list(want)} tensor")
+    return lse
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: float | None = None, out_dtype: torch.dtype | None = None,
         out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
@@ -112,21 +147,25 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
 
     Returns (O, LSE); LSE is float32 [B,Hq,N] (None if ``lse`` is False).
     """
-    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dims(t, 4, name)
     B, Hq, N, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
+    _shape(k, (B, Hkv, Nk, d), "k")
+    _shape(v, (B, Hkv, Nk, d), "v")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share a dtype")
+    _dtype_code(q.dtype)
+    if out is not None:
+        _shape(out, (B, Hq, N, d), "out")
+        _dtype_code(out.dtype)
+    _on_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse if isinstance(lse, torch.Tensor) else None))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=out_dtype or q.dtype, device=q.device)
-    if lse is True:
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N)):
-        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    lse = _lse_arg(lse, (B, Hq, N), q.device)
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                     lse.data_ptr() if lse is not None else None,
                     B, Hq, Hkv, N, Nk, d, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
@@ -151,25 +190,28 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
 
     Returns (O [total,Hq,d], LSE float32 [Hq,total] or None).
     """
-    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dims(t, 3, name)
     total, Hq, d = q.shape
     Hkv = k.shape[1]
     if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must be bfloat16")
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
-        raise ValueError("cu_seqlens must be a contiguous int32 vector")
-    if k.shape[0] != total or v.shape[0] != total:
-        raise ValueError("q, k and v must hold the same packed tokens")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous int32 vector of batch + 1 >= 2 entries")
+    _shape(k, (total, Hkv, d), "k")
+    _shape(v, (total, Hkv, d), "v")
+    if out is not None:
+        _shape(out, (total, Hq, d), "out")
+        _dtype_code(out.dtype)
+    _on_gpu(("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens), ("out", out),
+            ("lse", lse if isinstance(lse, torch.Tensor) else None))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((total, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    if lse is True:
-        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (Hq, total)):
-        raise ValueError("lse must be a contiguous float32 [Hq, total] tensor")
+    lse = _lse_arg(lse, (Hq, total), q.device)
     st = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr() if lse is not None else None, cu_seqlens.data_ptr(),
                            cu_seqlens.numel() - 1, Hq, Hkv, total, int(max_seqlen), d,
@@ -186,18 +228,28 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
         dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Backward of ``fwd``. q, dout [B,Hq,N,d] bf16 and o (bf16 or float32) sharing element strides;
     k, v [B,Hkv,Nk,d] bf16 sharing strides; lse float32 [B,Hq,N] from ``fwd``. Returns (dq, dk, dv)."""
-    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dims(t, 4, name)
     B, Hq, N, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
+    _shape(k, (B, Hkv, Nk, d), "k")
     for t in (q, k, v, dout):
         if t.dtype != torch.bfloat16:
             raise ValueError("q, k, v and dout must be bfloat16")
+    _dtype_code(o.dtype)
     if o.stride() != q.stride() or dout.stride() != q.stride() or o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("o and dout must share q's shape and strides")
     if v.stride() != k.stride() or v.shape != k.shape:
         raise ValueError("v must share k's shape and strides")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    for name, t, want in (("dq", dq, (B, Hq, N, d)), ("dk", dk, (B, Hkv, Nk, d)), ("dv", dv, (B, Hkv, Nk, d))):
+        if t is not None:
+            _shape(t, want, name)
+            _dtype_code(t.dtype)
+    _on_gpu(("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq), ("dk", dk),
+            ("dv", dv), ("workspace", workspace))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     gdt = grad_dtype or torch.bfloat16
@@ -221,15 +273,19 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
 def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None = None) -> dict:
     """FP8 quantiser. q [B,Hq,N,128], k/v [B,Hkv,N,128] bf16 (k and v sharing strides); signs a
     float32 [128] tensor of +-1 on the GPU (None: no rotation). Returns the e4m3 tensors and scales."""
-    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dims(t, 4, name)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
+    _shape(k, (B, Hkv, N, d), "k")
     if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must be bfloat16")
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
     if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_contiguous()):
         raise ValueError("signs must be a contiguous float32 vector of head_dim entries")
+    _on_gpu(("q", q), ("k", k), ("v", v), ("signs", signs))
+    lib = load()
     f8, dev = torch.float8_e4m3fn, q.device
     npad = -(-N // 64) * 64
     out = dict(q8=torch.empty((B, Hq, N, d), dtype=f8, device=dev),
@@ -249,19 +305,32 @@ def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, signs: torch
 def fwd_fp8(quant: dict, causal: bool = False, scale: float | None = None, out_dtype: torch.dtype = torch.bfloat16,
             out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
     """FP8 prefill on ``fp8_quantize``'s outputs. Returns (O [B,Hq,N,128], LSE float32 [B,Hq,N])."""
-    lib = load()
+    _dims(quant["q8"], 4, "q8")
     B, Hq, N, d = quant["q8"].shape
     Hkv = quant["k8"].shape[1]
+    npad = -(-N // 64) * 64
+    for name, want in (("k8", (B, Hkv, N, d)), ("v8t", (B, Hkv, d, npad)), ("q_scale", (B, Hq, -(-N // 128))),
+                       ("k_scale", (B, Hkv, npad // 64)), ("v_scale", (B, Hkv))):
+        _shape(quant[name], want, name)
+    for name in ("q8", "k8", "v8t"):
+        if quant[name].dtype != torch.float8_e4m3fn or not quant[name].is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float8_e4m3fn tensor")
+    for name in ("q_scale", "k_scale", "v_scale"):
+        if quant[name].dtype != torch.float32 or not quant[name].is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if out is not None:
+        _shape(out, (B, Hq, N, d), "out")
+        _dtype_code(out.dtype)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    _on_gpu(*((n, quant[n]) for n in ("q8", "k8", "v8t", "q_scale", "k_scale", "v_scale")), ("out", out),
+            ("lse", lse if isinstance(lse, torch.Tensor) else None))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=quant["q8"].device)
-    if not out.is_contiguous():
-        raise ValueError("out must be contiguous")
-    if lse is True:
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=out.device)
-    elif lse is False:
-        lse = None
+    lse = _lse_arg(lse, (B, Hq, N), out.device)
     st = lib.fa_fwd_fp8(quant["q8"].data_ptr(), quant["k8"].data_ptr(), quant["v8t"].data_ptr(),
                         quant["q_scale"].data_ptr(), quant["k_scale"].data_ptr(), quant["v_scale"].data_ptr(),
                         out.data_ptr(), lse.data_ptr() if lse is not None else None, B, Hq, Hkv, N, d,
@@ -271,8 +340,9 @@ def fwd_fp8(quant: dict, causal: bool = False, scale: float | None = None, out_d
     return out, lse
 
 
-def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seqlen: int, head_dim: int) -> int:
-    return int(load().fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim))
+def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seqlen: int, head_dim: int,
+                           split_tokens: int = 0) -> int:
+    return int(load().fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim, split_tokens))
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
@@ -280,24 +350,33 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
            out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
            workspace: torch.Tensor | None = None):
     """Split-KV decode. q [B,Hq,d] bf16; caches [B,Hkv,Lmax,d] bf16; seqlens int32 [B] on the GPU."""
-    lib = load()
+    _dims(q, 3, "q")
+    _dims(k_cache, 4, "k_cache")
     B, Hq, d = q.shape
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, (B, Hkv, Lmax, d), "k_cache")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must be bfloat16")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must share shape and strides")
     if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
         raise ValueError("seqlens must be a contiguous int32 tensor of length batch")
+    if out is not None:
+        _shape(out, (B, Hq, d), "out")
+        _dtype_code(out.dtype)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    _on_gpu(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens), ("out", out),
+            ("lse", lse if isinstance(lse, torch.Tensor) else None), ("workspace", workspace))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.bfloat16, device=q.device)
-    if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
-    need = decode_workspace_bytes(B, Hq, Hkv, Lmax, d)
+    lse = _lse_arg(lse, (B, Hq), q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, Lmax, d, split_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
@@ -307,6 +386,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
                        _stream(q.device))
     _check(st)
     return out, lse
+
 
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
@@ -320,9 +400,13 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     Hkv, d] is passed as ``pool.transpose(1, 2)``); block_table int32
     [B, max_blocks]; seqlens int32 [B]; all on the GPU.
     """
-    lib = load()
+    _dims(q, 3, "q")
+    _dims(k_pages, 4, "k_pages")
     B, Hq, d = q.shape
     P, Hkv, ps = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _shape(k_pages, (P, Hkv, ps, d), "k_pages")
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise ValueError("q and the pages must be bfloat16")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     if k_pages.stride() != v_pages.stride() or k_pages.shape != v_pages.shape:
@@ -333,15 +417,21 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
         raise ValueError("seqlens must be a contiguous int32 tensor of length batch")
     max_blocks = block_table.shape[1]
+    if out is not None:
+        _shape(out, (B, Hq, d), "out")
+        _dtype_code(out.dtype)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    _on_gpu(("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+            ("seqlens", seqlens), ("out", out), ("lse", lse if isinstance(lse, torch.Tensor) else None),
+            ("workspace", workspace))
+    lib = load()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.bfloat16, device=q.device)
-    if lse is True:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
-    need = decode_workspace_bytes(B, Hq, Hkv, max_blocks * ps, d)
+    lse = _lse_arg(lse, (B, Hq), q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, max_blocks * ps, d, split_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),

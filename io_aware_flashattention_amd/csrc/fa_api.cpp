@@ -69,7 +69,8 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
     if (page_stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: strides must be non-negative");
   if ((int64_t)max_blocks_per_seq * page_size > 0x7fffffffLL - 64)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_paged: max_blocks_per_seq * page_size overflows int32");
-  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d not supported (128)", head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d not supported (64 or 128)", head_dim);
   if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
     return fail(FA_ERR_UNSUPPORTED,
                 "fa_decode_paged: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head",
@@ -83,7 +84,7 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
   if ((int64_t)page_size * page_stride[2] >= (int64_t(1) << 31))
     return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: page_size * slot stride must stay below 2^31 elements");
   const int max_seqlen = max_blocks_per_seq * page_size;
-  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim);
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen, head_dim, split_tokens);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace of %zu bytes needed, %zu given", need,
                 workspace_bytes);
@@ -433,44 +434,60 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
 }
 
 size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                 int32_t max_seqlen_k, int32_t head_dim) {
+                                 int32_t max_seqlen_k, int32_t head_dim, int32_t split_tokens) {
   if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || max_seqlen_k <= 0 || head_dim <= 0) return 0;
   if (heads_q % heads_kv != 0) return 0;
-  // one partial (G heads x (d + 1) floats) per (slab, wave) piece: at most B*Hkv + W
+  // One partial (G heads x (d + 1) floats) per piece, a piece being the part
+  // of one (sequence, kv head) slab inside one wave's range. The W ranges cut
+  // the stream of B*Hkv slabs at no more than W - 1 interior points, so there
+  // are at most B*Hkv + W pieces whatever split_tokens is: a larger split only
+  // leaves some waves without a range. The bound is the same for every split.
+  (void)split_tokens;
   const int64_t parts = (int64_t)batch * heads_kv + fa::decode_waves();
   return static_cast<size_t>(parts * (heads_q / heads_kv) * (head_dim + 1) * 4);
 }
 
-fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* seqlens_k, void* o, float* lse,
-                      int32_t batch, int32_t heads_q, int32_t heads_kv,
-                      int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
-                      fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
-                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !kv_stride)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: q, caches, seqlens_k, o and kv_stride must be non-null");
-  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || max_seqlen_k <= 0 || head_dim <= 0)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: sizes must be positive");
-  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: softmax_scale must be finite and positive (got %g)", (double)softmax_scale);
-  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: unknown out_dtype %d", (int)out_dtype);
-  for (int i = 0; i < 3; ++i)
-    if (kv_stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: strides must be non-negative");
-  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "fa_decode: head_dim %d not supported (128)", head_dim);
-  if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head",
-                heads_q, heads_kv);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode: q, caches, o and workspace must be 16-byte aligned");
-  for (int i = 0; i < 3; ++i)
-    if (kv_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "fa_decode: kv strides must be multiples of 8 elements");
-  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen_k, head_dim);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if ((int64_t)batch * heads_q > 0x7fffffffLL / 4)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode: problem too large for one launch");
+}  // extern "C"
 
+namespace {
+
+// Argument checks of fa_decode (everything but the workspace), run before
+// anything touches the GPU.
+fa_status_t decode_checks(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seqlens_k, const void* o, int32_t batch, int32_t heads_q,
+                          int32_t heads_kv, int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                          fa_dtype_t out_dtype, float softmax_scale) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !kv_stride)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, caches, seqlens_k, o and kv_stride must be non-null", fn);
+  if (batch <= 0 || heads_q <= 0 || heads_kv <= 0 || max_seqlen_k <= 0 || head_dim <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", fn);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite and positive (got %g)", fn,
+                (double)softmax_scale);
+  if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: unknown out_dtype %d", fn, (int)out_dtype);
+  for (int i = 0; i < 3; ++i)
+    if (kv_stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s: strides must be non-negative", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+  if (heads_q % heads_kv != 0 || heads_q / heads_kv > 32)
+    return fail(FA_ERR_UNSUPPORTED,
+                "%s: heads_q (%d) must be a multiple of heads_kv (%d) with at most 32 query heads per kv head", fn,
+                heads_q, heads_kv);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(FA_ERR_UNSUPPORTED, "%s: q, caches and o must be 16-byte aligned", fn);
+  for (int i = 0; i < 3; ++i)
+    if (kv_stride[i] % 8) return fail(FA_ERR_UNSUPPORTED, "%s: kv strides must be multiples of 8 elements", fn);
+  if ((int64_t)batch * heads_q > 0x7fffffffLL / 4)
+    return fail(FA_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
+  return FA_OK;
+}
+
+fa_status_t decode_launch(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seqlens_k, void* o, float* lse, int32_t batch, int32_t heads_q,
+                          int32_t heads_kv, int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                          fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens, void* workspace,
+                          void* stream) {
   fa::DecodeParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.seqlens = seqlens_k; p.o = o; p.lse = lse;
   const int64_t parts = ((int64_t)batch * heads_kv + fa::decode_waves()) * (heads_q / heads_kv);
@@ -484,8 +501,30 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.scale_log2 = softmax_scale * kLog2e;
   p.out_fp32 = out_dtype == FA_DTYPE_FP32;
   hipError_t e = fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens_k, void* o, float* lse,
+                      int32_t batch, int32_t heads_q, int32_t heads_kv,
+                      int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                      fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const fa_status_t st = decode_checks("fa_decode", q, k_cache, v_cache, seqlens_k, o, batch, heads_q, heads_kv,
+                                       max_seqlen_k, head_dim, kv_stride, out_dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(workspace))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode: workspace must be 16-byte aligned");
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen_k, head_dim, split_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  return decode_launch("fa_decode", q, k_cache, v_cache, seqlens_k, o, lse, batch, heads_q, heads_kv, max_seqlen_k,
+                       head_dim, kv_stride, out_dtype, softmax_scale, split_tokens, workspace, stream);
 }
 
 }  // extern "C"

@@ -50,10 +50,8 @@ namespace fa {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int KB = 32;                       // keys per block
 constexpr int NST = FA_DEC_NST;
-constexpr int BLK = KB * D;                  // bf16 elements per K (or V) block
 constexpr float kRescaleThreshold = 8.f;
 static_assert(NST >= 2 && NST <= 4, "");
 
@@ -68,9 +66,15 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// swizzles of 256-byte rows (the bank model is described with the prefill kernel)
-__device__ __forceinline__ int kswz_d(int r) { return sigma32(r & 31) & 15; }
-__device__ __forceinline__ int vswz_d(int r) { return 4 * (r & 3); }
+// LDS swizzles of the 16-byte chunks of a K or V row (the bank model is
+// described with the prefill kernel): 256-byte rows (D = 128) fill a bank
+// line each, 128-byte rows (D = 64) share one between two rows
+template <int D> __device__ __forceinline__ int kswz_d(int r) {
+  return D == 128 ? (sigma32(r & 31) & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int vswz_d(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // Lengths and block-table entries are read at wave-uniform addresses through
 // the constant address space, so they become scalar loads: they wait on the
@@ -118,10 +122,14 @@ struct PageRun {
 
 namespace detail {
 
-template <typename TOut, bool PAGED>
+template <int D, typename TOut, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int BLK = KB * D;                // bf16 elements per K (or V) block
+  constexpr int NLD = BLK * 2 / 1024;        // 1-KB DMA writes per operand block (8 or 4)
+  constexpr int RPW = 32 / NLD;              // block rows per write (4 or 8)
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row (16 or 8)
   __shared__ __attribute__((aligned(16))) __bf16 smem[NST * 2 * BLK];      // [stage][K, V][BLK]
 
   const int lane = threadIdx.x;
@@ -198,20 +206,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     return true;
   };
 
-  // ---- DMA of one block: eight 1-KB writes per operand, rows past the piece clamped
-  const int drow = lane >> 4;                  // row of the lane's chunk, + 4 per write
-  const int dchunk = lane & 15;
+  // ---- DMA of one block: NLD 1-KB writes per operand, rows past the piece clamped
+  const int drow = lane / CPR;                 // row of the lane's chunk, + RPW per write
+  const int dchunk = lane % CPR;
   // byte offsets of the lane's K and V chunks in write i, from the block's
   // first row (whole blocks: contiguous, or page-aligned paged)
   // (32-bit: usable while 32 rows of the row or slot stride stay below 2^31 bytes)
   const bool lane_ok = p.kv_stride[2] < (int64_t(1) << 25);
   const bool fast_pages = PAGED && lane_ok && (p.page_size == 16 || p.page_size % KB == 0);
-  uint32_t lane_k[8], lane_v[8];
+  uint32_t lane_k[NLD], lane_v[NLD];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 4 * i + drow;
-    lane_k[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ kswz_d(r))));
-    lane_v[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ vswz_d(r))));
+  for (int i = 0; i < NLD; ++i) {
+    const int r = RPW * i + drow;
+    lane_k[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ kswz_d<D>(r))));
+    lane_v[i] = (uint32_t)(2 * ((int64_t)r * p.kv_stride[2] + 8 * (dchunk ^ vswz_d<D>(r))));
   }
   // Paged cache: table entries of the block at cursor c (scalar loads through
   // the constant address space; ids outside [0, num_pages) are clamped).
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
         asm("" : "+s"(b0), "+s"(b1));
         const intptr_t dvk = reinterpret_cast<intptr_t>(vp) - reinterpret_cast<intptr_t>(kp);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const char* base = i < 4 ? b0 : b1;
+        for (int i = 0; i < NLD; ++i) {
+          const char* base = i < NLD / 2 ? b0 : b1;
           __builtin_amdgcn_global_load_lds((const void*)(base + lane_k[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
           __builtin_amdgcn_global_load_lds((const void*)(base + dvk + lane_v[i]), (lds_void*)(dst + BLK + i * 512),
                                            16, 0, 0);
@@ -277,17 +285,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       const int rs = (int)p.kv_stride[2];
       const int o = pr.off + drow;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 4 * i + drow;
-        const int kr = min(o + 4 * i, pr.lim);             // slot counted from the first page
+      for (int i = 0; i < NLD; ++i) {
+        const int r = RPW * i + drow;
+        const int kr = min(o + RPW * i, pr.lim);           // slot counted from the first page
         const bool c1 = kr >= ps, c2 = kr >= 2 * ps;
         int slot = c1 ? kr - ps : kr;
         slot = c2 ? slot - ps : slot;
         const __bf16* row = (c2 ? k2 : c1 ? k1 : k0) + (uint32_t)(slot * rs);
         const __bf16* vrow = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(row) + dvk);
-        __builtin_amdgcn_global_load_lds((const void*)(row + 8 * (dchunk ^ kswz_d(r))), (lds_void*)(dst + i * 512),
+        __builtin_amdgcn_global_load_lds((const void*)(row + 8 * (dchunk ^ kswz_d<D>(r))), (lds_void*)(dst + i * 512),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (dchunk ^ vswz_d(r))),
+        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (dchunk ^ vswz_d<D>(r))),
                                          (lds_void*)(dst + BLK + i * 512), 16, 0, 0);
       }
     } else {
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
         asm("" : "+s"(b0));
         const intptr_t dvk = reinterpret_cast<intptr_t>(vp) - reinterpret_cast<intptr_t>(kp);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NLD; ++i) {
           __builtin_amdgcn_global_load_lds((const void*)(b0 + lane_k[i]), (lds_void*)(dst + i * 512), 16, 0, 0);
           __builtin_amdgcn_global_load_lds((const void*)(b0 + dvk + lane_v[i]), (lds_void*)(dst + BLK + i * 512), 16,
                                            0, 0);
@@ -307,12 +315,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       const int64_t base = (int64_t)c.b * p.kv_stride[0] + (int64_t)c.kvh * p.kv_stride[1];
       const int last = c.end - 1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 4 * i + drow;
+      for (int i = 0; i < NLD; ++i) {
+        const int r = RPW * i + drow;
         const int64_t row = base + (int64_t)min(c.pos + r, last) * p.kv_stride[2];
-        __builtin_amdgcn_global_load_lds((const void*)(kp + row + 8 * (dchunk ^ kswz_d(r))),
+        __builtin_amdgcn_global_load_lds((const void*)(kp + row + 8 * (dchunk ^ kswz_d<D>(r))),
                                          (lds_void*)(dst + i * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vp + row + 8 * (dchunk ^ vswz_d(r))),
+        __builtin_amdgcn_global_load_lds((const void*)(vp + row + 8 * (dchunk ^ vswz_d<D>(r))),
                                          (lds_void*)(dst + BLK + i * 512), 16, 0, 0);
       }
     }
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   {
     const int r = sigma32(r32);
 #pragma unroll
-    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz_d(r));
+    for (int kc = 0; kc < KSTEPS; ++kc) koff[kc] = r * D + 8 * ((2 * kc + half) ^ kswz_d<D>(r));
   }
   int voff[DBLK];
   {
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const int col = 32 * db + 16 * (gg & 1) + 4 * (i & 3);
-      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_d(r)) + (col & 7);
+      voff[db] = r * D + 8 * ((col >> 3) ^ vswz_d<D>(r)) + (col & 7);
     }
   }
 
@@ -365,9 +373,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       if (dma_ok) dma_pages = pages_of(dma); // table entries for the next issue
     }
     const int ahead = issued - blk - 1;        // blocks allowed to stay in flight
-    if (ahead >= 3) wait_vmcnt<48>();
-    else if (ahead == 2) wait_vmcnt<32>();
-    else if (ahead == 1) wait_vmcnt<16>();
+    if (ahead >= 3) wait_vmcnt<6 * NLD>();
+    else if (ahead == 2) wait_vmcnt<4 * NLD>();
+    else if (ahead == 1) wait_vmcnt<2 * NLD>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -476,8 +484,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
 // One wave per (b, query head): LSE = log sum_s exp(lse_s), O = sum_s
 // exp(lse_s - LSE) o_s over the pieces s of the head's slab.
-template <typename TOut>
+template <int D, typename TOut>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
+  constexpr int EPL = D / 64;                  // output elements per lane (2 or 1)
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)p.batch * p.heads_q) return;
@@ -502,10 +511,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   T = uniform64(T) * p.heads_kv;
   before = uniform64(before);
   const int L = seq_len(p, b);
-  TOut* op = reinterpret_cast<TOut*>(p.o) + row * D + 2 * lane;
+  TOut* op = reinterpret_cast<TOut*>(p.o) + row * D + EPL * lane;
   if (L == 0) {                                // no key: O = 0, LSE = -inf
-    op[0] = (TOut)0.f;
-    op[1] = (TOut)0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) op[e] = (TOut)0.f;
     if (p.lse != nullptr && lane == 0) p.lse[row] = kNegInf;
     return;
   }
@@ -515,18 +524,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const int slab = b * p.heads_kv + kvh;
   float mx = kNegInf;
   for (int w = w0; w <= w1; ++w) mx = fmaxf(mx, p.part_lse[(int64_t)(slab + w) * G + g]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  float den = 0.f, n[EPL] = {};
   for (int w = w0; w <= w1; ++w) {
     const int64_t part = (int64_t)(slab + w) * G + g;
     const float wt = __expf(p.part_lse[part] - mx);
-    const float2 v = *reinterpret_cast<const float2*>(p.part_o + part * D + 2 * lane);
+    const float* v = p.part_o + part * D + EPL * lane;
     den += wt;
-    n0 = fmaf(wt, v.x, n0);
-    n1 = fmaf(wt, v.y, n1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) n[e] = fmaf(wt, v[e], n[e]);
   }
   const float inv = 1.f / den;
-  op[0] = (TOut)(n0 * inv);
-  op[1] = (TOut)(n1 * inv);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) op[e] = (TOut)(n[e] * inv);
   if (p.lse != nullptr && lane == 0) p.lse[row] = mx + __logf(den);
 }
 
@@ -534,16 +543,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
 
 namespace {
 
-template <typename TOut>
+template <int D, typename TOut>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   if (p.block_table != nullptr)
-    hipLaunchKernelGGL((detail::decode_split_kernel<TOut, true>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((detail::decode_split_kernel<D, TOut, true>), dim3((unsigned)p.n_waves), dim3(64), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((detail::decode_split_kernel<TOut, false>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((detail::decode_split_kernel<D, TOut, false>), dim3((unsigned)p.n_waves), dim3(64), 0, stream,
+                       p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.heads_q;
-  hipLaunchKernelGGL((detail::decode_merge_kernel<TOut>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((detail::decode_merge_kernel<D, TOut>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
@@ -552,7 +564,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 int decode_waves() { return 256 * FA_DEC_WPC; }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  return p.out_fp32 ? launch_t<float>(p, stream) : launch_t<__bf16>(p, stream);
+  if (p.head_dim == 64) return p.out_fp32 ? launch_t<64, float>(p, stream) : launch_t<64, __bf16>(p, stream);
+  return p.out_fp32 ? launch_t<128, float>(p, stream) : launch_t<128, __bf16>(p, stream);
 }
 
 }  // namespace fa

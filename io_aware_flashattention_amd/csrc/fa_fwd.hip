@@ -35,37 +35,18 @@
 //     weights that actually enter P V (an exactly normalised combination of V
 //     rows), and the log-sum-exp uses the float32 sum of the weights.
 #include <algorithm>
+#include <atomic>
 
 #include "fa_device.h"
 #include "fa_launch.h"
-
-#ifndef FA_FWD_NW128
-#define FA_FWD_NW128 8       // waves per workgroup at head_dim 128
-#endif
-#ifndef FA_FWD_STAGES128
-#define FA_FWD_STAGES128 3   // K/V tiles resident or in flight at head_dim 128
-#endif
-#ifndef FA_FWD_PP128
-#define FA_FWD_PP128 1       // ping-pong kernel for head_dim 128
-#endif
-#ifndef FA_FWD_PPST
-#define FA_FWD_PPST 3        // its K/V ring depth
-#endif
-#ifndef FA_FWD_PRIO
-#define FA_FWD_PRIO 0        // raise wave priority during matrix-core units
-#endif
-#ifndef FA_FWD_AHEAD
-#define FA_FWD_AHEAD 4       // fragment-read steps issued ahead of their MFMA
-#endif
-#ifndef FA_FWD_R128
-#define FA_FWD_R128 1        // 32-row blocks per wave at head_dim 128
-#endif
 
 namespace fa {
 
 namespace {
 
 constexpr int BC = 64;       // keys per tile
+constexpr int kPpStages = 3; // K/V ring depth of the ping-pong kernel
+constexpr int kAhead = 4;    // its fragment-read steps issued ahead of their MFMA
 constexpr float kRescaleThreshold = 8.f;
 
 // LDS swizzles, measured against gfx950's 64 banks x 4 bytes: a ds_read_b128
@@ -835,7 +816,7 @@ void fwd_pp_kernel(const FwdParams p) {
   // keeps that order): K for the 8 score k-steps, then V (two transposing
   // reads per PV MFMA) for the 16 PV MFMAs.
   auto gunit = [&](int SK, int SV) __attribute__((always_inline)) {
-    constexpr int AHEAD = FA_FWD_AHEAD;
+    constexpr int AHEAD = kAhead;
     const __bf16* ks = smem + SK * 2 * TILE;
     const __bf16* vs = smem + SV * 2 * TILE + TILE;
     bf16x8 kf[KSTEPS][2];
@@ -1019,17 +1000,11 @@ void fwd_pp_kernel(const FwdParams p) {
         const int j = (u >> 1) - 1;
         constexpr int SK = (r / 2) % STAGES;          // stage of tile j + 1
         constexpr int SV = (r / 2 + STAGES - 1) % STAGES;     // stage of tile j
-#if FA_FWD_PRIO
-        __builtin_amdgcn_s_setprio(1);
-#endif
         if (j >= lo_w && j + 1 < nt_w) gunit(SK, SV);
         else {
           if (j + 1 >= lo_w && j + 1 < nt_w) scores(SK);
           if (j >= lo_w && j < nt_w) accumulate(SV);
         }
-#if FA_FWD_PRIO
-        __builtin_amdgcn_s_setprio(0);
-#endif
       }
       phase_end(ph, nph);
       return true;
@@ -1108,17 +1083,19 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (the persistent grid's size).
+// Compute units of the current device (the persistent grid's size), looked
+// up once per device. Concurrent first calls may both query the runtime; each
+// stores the same value, and the relaxed atomics make that race-free.
 inline int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D, bool CAUSAL, typename TOut, int STAGES>
@@ -1152,16 +1129,11 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.in_fp32) return launch_fwd_f32(p, stream);
   if (p.head_dim == 64)
     return p.causal ? launch_out<64, true, 4, 1, 3>(p, stream) : launch_out<64, false, 4, 1, 3>(p, stream);
-#if FA_FWD_PP128
   if (p.causal)
-    return p.out_fp32 ? launch_pp<128, true, float, FA_FWD_PPST>(p, stream)
-                      : launch_pp<128, true, __bf16, FA_FWD_PPST>(p, stream);
-  return p.out_fp32 ? launch_pp<128, false, float, FA_FWD_PPST>(p, stream)
-                    : launch_pp<128, false, __bf16, FA_FWD_PPST>(p, stream);
-#else
-  return p.causal ? launch_out<128, true, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream)
-                  : launch_out<128, false, FA_FWD_NW128, FA_FWD_R128, FA_FWD_STAGES128>(p, stream);
-#endif
+    return p.out_fp32 ? launch_pp<128, true, float, kPpStages>(p, stream)
+                      : launch_pp<128, true, __bf16, kPpStages>(p, stream);
+  return p.out_fp32 ? launch_pp<128, false, float, kPpStages>(p, stream)
+                    : launch_pp<128, false, __bf16, kPpStages>(p, stream);
 }
 
 }  // namespace fa

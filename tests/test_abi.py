@@ -221,7 +221,8 @@ def _dec(**kw):
     (dict(kvs=None), 1, "non-null"),
     (dict(L=0), 1, "positive"),
     (dict(scale=float("inf")), 1, "softmax_scale"),
-    (dict(d=64), 2, "head_dim"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(d=256), 2, "head_dim"),
     (dict(Hq=16, Hkv=3), 2, "multiple"),
     (dict(Hq=66, Hkv=1), 2, "at most 32"),
     (dict(k=FAKE + 4), 2, "aligned"),
@@ -257,7 +258,7 @@ def _paged(**kw):
     (dict(pst=(-4096, 2048, 128)), 1, "non-negative"),
     (dict(mb=1 << 27, ps=32), 1, "overflows"),
     (dict(outd=3), 1, "out_dtype"),
-    (dict(d=64), 2, "head_dim"),
+    (dict(d=96), 2, "head_dim"),
     (dict(Hq=16, Hkv=3), 2, "multiple"),
     (dict(ps=8), 2, "page_size"),
     (dict(v=FAKE + 0x200004), 2, "aligned"),
@@ -273,13 +274,25 @@ def test_decode_paged_rejects_before_launch(kw, status, needle):
 
 def test_decode_workspace_size():
     lib = _lib.load()
-    waves = lib.fa_decode_workspace_bytes(1, 1, 1, 100, 128) // (129 * 4) - 1   # decode grid size
+    waves = lib.fa_decode_workspace_bytes(1, 1, 1, 100, 128, 0) // (129 * 4) - 1   # decode grid size
     assert waves > 0
-    # (batch * heads_kv + waves) pieces, each heads_q / heads_kv heads of (128 + 1) floats
-    assert lib.fa_decode_workspace_bytes(64, 64, 8, 32768, 128) == (64 * 8 + waves) * 8 * 129 * 4
-    assert lib.fa_decode_workspace_bytes(2, 8, 8, 1000, 128) == (16 + waves) * 129 * 4
-    assert lib.fa_decode_workspace_bytes(0, 1, 1, 100, 128) == 0
-    assert lib.fa_decode_workspace_bytes(1, 6, 4, 100, 128) == 0
+    # (batch * heads_kv + waves) pieces, each heads_q / heads_kv heads of (d + 1) floats,
+    # whatever split_tokens is (a larger split leaves waves without a range)
+    for split in (0, 1, 256, 4096, 1 << 20):
+        assert lib.fa_decode_workspace_bytes(64, 64, 8, 32768, 128, split) == (64 * 8 + waves) * 8 * 129 * 4
+        assert lib.fa_decode_workspace_bytes(8, 12, 12, 1024, 64, split) == (8 * 12 + waves) * 65 * 4
+    assert lib.fa_decode_workspace_bytes(2, 8, 8, 1000, 128, 0) == (16 + waves) * 129 * 4
+    assert lib.fa_decode_workspace_bytes(0, 1, 1, 100, 128, 0) == 0
+    assert lib.fa_decode_workspace_bytes(1, 6, 4, 100, 128, 0) == 0
+
+
+def test_decode_accepts_head_dim_64_up_to_the_workspace_check():
+    """d = 64 passes every argument check; with a too-small workspace the call
+    then stops at that check, still before any launch."""
+    st, msg = _dec(d=64, kvs=(2 * 4096 * 64, 4096 * 64, 64), wsb=16)
+    assert st == 3 and "workspace" in msg, msg
+    st, msg = _paged(d=64, pst=(2 * 16 * 64, 16 * 64, 64), wsb=16)
+    assert st == 3 and "workspace" in msg, msg
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):

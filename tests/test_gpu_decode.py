@@ -145,3 +145,29 @@ def test_huge_row_stride_takes_the_general_path():
     del pools
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lo,hi", [(8, 12, 12, 1, 1024), (16, 32, 4, 100, 5000)],
+                         ids=["gpt2_small_12x64", "gqa_32x4"])
+def test_decode_head_dim_64(B, Hq, Hkv, lo, hi):
+    """Decode at head_dim 64: GPT-2-small's heads (12 of 64, one kv head each,
+    contexts of 1..1024 tokens, the pages' GPT-2 workload shape) and a GQA mix.
+    Full oracle comparison for several split sizes; the paged form of the same
+    cache (16-token pages, token-major, shuffled table) returns the same bits;
+    NaN sits past every length in both."""
+    cfg = W.DecodeConfig(f"d64_B{B}_Hq{Hq}_Hkv{Hkv}", B, Hq, Hkv, lo, hi, 64, 5100 + Hq)
+    q, kc, vc, lens = W.make_decode_inputs(cfg, pad="nan")
+    o_ref, l_ref = decode_ref(W.to_f64(q), W.to_f64(kc), W.to_f64(vc), lens, cfg.scale)
+    qd, kd, vd, ld = to_dev(q), to_dev(kc), to_dev(vc), torch.from_numpy(lens).to("cuda")
+    _, kp, vp, table, _ = W.make_paged_decode_inputs(cfg, 16, layout="token", pad="nan", lengths=lens)
+    kpd, vpd, tab = to_dev(kp).transpose(1, 2), to_dev(vp).transpose(1, 2), torch.from_numpy(table).to("cuda")
+    for split in (0, 64, 1000):
+        say(f"case {cfg.name} split={split} sum(L)={int(lens.sum())}")
+        o32, l32 = fa().decode(qd, kd, vd, ld, scale=cfg.scale, split_tokens=split, out_dtype=torch.float32)
+        o16, _ = fa().decode(qd, kd, vd, ld, scale=cfg.scale, split_tokens=split, out_dtype=torch.bfloat16)
+        op, lp = fa().decode_paged(qd, kpd, vpd, tab, ld, scale=cfg.scale, split_tokens=split,
+                                   out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        check(o32, l32, o_ref, l_ref, f"{cfg.name} split={split}")
+        assert torch.equal(o16, o32.to(torch.bfloat16))
+        assert torch.equal(op, o32) and torch.equal(lp, l32), "paged and contiguous decode differ"

@@ -1,4 +1,13 @@
-"""GPU parity of the FP8 path (fa_fp8_quantize, fa_fwd_fp8) against oracle/fp8.py.
+"""GPU parity of the FP8 path (fa_fp8_quantize, fa_fwd_fp8) against exact fp64
+attention and against oracle/fp8.py.
+
+Against exact attention (the gate the pages ask of any FP8 attention): the
+error model of tests/fp8_gate.py, derived from e4m3's 3-bit mantissa,
+predicts per element how far e4m3 rounding of Q, K, V and the weights can
+move O and the LSE; the kernel's rms error may not exceed the model's, and
+no element may lie beyond 8 predicted standard deviations.
+
+Against the FP8 oracle (the method's own steps in fp64):
 
 The quantiser decides its codes in float32 exactly as the oracle does (same
 butterfly order, same scale formula, nearest-even e4m3), so codes and scales
@@ -18,6 +27,7 @@ import torch
 
 from io_aware_flashattention_amd import workloads as W
 from oracle import attention_ref, fp8_attention_ref, quantize
+from tests import fp8_gate
 from tests.parity import say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -89,13 +99,19 @@ def test_fp8_attention_matches_oracle(N, causal):
     quant = quantize(W.to_f64(q), W.to_f64(k), W.to_f64(v), signs)
     o_ref, l_ref = fp8_attention_ref(quant, 1 / np.sqrt(128), causal=causal)
     _check(o, lse, o_ref, l_ref, f"fp8 N={N} causal={causal}")
-    o_ex, _ = attention_ref(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / np.sqrt(128), causal=causal)
-    say(f"  (against exact attention: O mean {np.abs(o.cpu().numpy() - o_ex).mean():.3e})")
+    q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    o_ex, l_ex = attention_ref(q64, k64, v64, 1 / np.sqrt(128), causal=causal)
+    so, sl = fp8_gate.error_model(q64, k64, v64, signs, 1 / np.sqrt(128), causal)
+    fp8_gate.gate(o.cpu().numpy(), lse.cpu().numpy(), o_ex, l_ex, so, sl, f"fp8 N={N} causal={causal}", say=say)
 
 
 def test_fp8_long_context_gqa_sampled():
     """The long-context GQA workload (64 query / 8 kv heads, 8192 tokens, 1% of
-    K rows x8), causal, on sampled rows of every head."""
+    K rows x8), causal, on sampled rows of every head: the first and last rows,
+    both sides of every kind of tile edge (64-key tiles, 128-row scale blocks,
+    256-row groups), rows that sit on a x8 key of some kv head and the row after
+    it, and a few more. Checked against the FP8 oracle and against exact
+    attention through the e4m3 error model."""
     cfg = W.CONFIGS["c4a_gqa_8k"]
     say(f"case fp8 {cfg.name} sampled rows")
     q, k, v = W.make_prefill_inputs(cfg)
@@ -103,8 +119,20 @@ def test_fp8_long_context_gqa_sampled():
     got = gpu_quant(q, k, v, signs)
     o, lse = fa().fwd_fp8(got, causal=True, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
-    quant = quantize(W.to_f64(q), W.to_f64(k), W.to_f64(v), signs)
+    N = cfg.seqlen
+    rows = {0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 4095, 4096, 4097, N - 129, N - 128, N - 65, N - 64,
+            N - 2, N - 1}
+    for kvh in range(cfg.heads_kv):
+        heavy = W.heavy_rows(cfg, 0, kvh)
+        rows |= {int(x) for x in heavy[:3]} | {int(x) + 1 for x in heavy[:3] if x + 1 < N} | {int(heavy[-1])}
+    rows |= set(np.random.default_rng(cfg.seed).integers(0, N, 8).tolist())
+    rows = sorted(rows)
+    q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    quant = quantize(q64, k64, v64, signs)
     o_ref, l_ref = fp8_attention_ref(quant, cfg.scale, causal=True, rows=rows)
-    _check(o[:, :, rows], lse[:, :, rows], o_ref[:, :, rows], l_ref[:, :, rows], f"fp8 {cfg.name}")
+    o_h, l_h = o[:, :, rows].cpu().numpy(), lse[:, :, rows].cpu().numpy()
+    _check(o[:, :, rows], lse[:, :, rows], o_ref[:, :, rows], l_ref[:, :, rows], f"fp8 {cfg.name} [{len(rows)} rows]")
+    o_ex, l_ex = attention_ref(q64[:, :, rows], k64, v64, cfg.scale, causal=True, q_positions=np.array(rows))
+    so, sl = fp8_gate.error_model(q64, k64, v64, signs, cfg.scale, True, rows=rows)
+    fp8_gate.gate(o_h, l_h, o_ex, l_ex, so, sl, f"fp8 {cfg.name} [{len(rows)} rows]", say=say)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
