@@ -203,6 +203,35 @@ FA_API fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_c
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. The arguments, the kernels and the result are
+ * fa_decode's (on the same inputs the two return identical bits); only the
+ * partials workspace differs: it is a static array inside the library, 16 MiB
+ * on each GPU the library runs on, held until the process ends. Nothing is
+ * allocated or freed by this call.
+ *
+ * Limit: fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen_k,
+ * head_dim, split_tokens) must not exceed 16 MiB (16777216 bytes); larger
+ * sizes return FA_ERR_UNSUPPORTED before anything is launched. (The bench's
+ * 64 sequences x 64 query heads over 8 kv heads at head_dim 128 need about
+ * 5.3 MB.)
+ *
+ * All calls on one GPU share that GPU's array and nothing in it needs to start
+ * at zero (every partial the merge reads is written first by the same call).
+ * Two calls whose kernels overlap on one GPU race on it: order them (one
+ * stream, or events), or use fa_decode with separate workspaces. The first
+ * call on a device looks up the array's device address (hipGetSymbolAddress);
+ * a failure there returns FA_ERR_HIP.
+ */
+FA_API fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seqlens_k, void* o, float* lse,
+                                     int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                     int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                                     fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens,
+                                     void* stream);
+
+/*
  * fa_decode_paged -- fa_decode against a paged KV cache: the cache lives in
  * fixed-size pages that need not be contiguous or in order, and a block table
  * maps each sequence's logical blocks of page_size tokens to physical pages

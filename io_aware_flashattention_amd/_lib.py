@@ -22,8 +22,9 @@ FA_MASK_NONE, FA_MASK_CAUSAL = 0, 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_HIP"}
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd_workspace_bytes", "fa_bwd", "fa_fp8_quantize", "fa_fwd_fp8",
-            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged", "fa_status_string",
+            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_noalloc", "fa_decode_paged", "fa_status_string",
             "fa_last_error_message")
+DECODE_SCRATCH_BYTES = 16 << 20      # the static workspace behind fa_decode_noalloc
 
 _i32, _i64p, _vp = ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
 _lib = None
@@ -70,6 +71,9 @@ def load():
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
                               ctypes.c_int, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
+    lib.fa_decode_noalloc.restype = ctypes.c_int
+    lib.fa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64p,
+                                      ctypes.c_int, ctypes.c_float, _i32, _vp]
     lib.fa_decode_paged.restype = ctypes.c_int
     lib.fa_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,      # q, k/v pages, table, seqlens, o, lse
                                     _i32, _i32, _i32, _i32,                  # batch, heads_q, heads_kv, head_dim
@@ -388,6 +392,43 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
     return out, lse
 
 
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
+                   out: torch.Tensor, lse: torch.Tensor | None = None, scale: float | None = None,
+                   split_tokens: int = 0):
+    """``decode`` through fa_decode_noalloc: the partials live in the library's
+    static scratch, so the library allocates nothing; the caller passes the
+    output (and optionally the LSE) tensors, so this wrapper allocates nothing
+    either."""
+    _dims(q, 3, "q")
+    _dims(k_cache, 4, "k_cache")
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, (B, Hkv, Lmax, d), "k_cache")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must be bfloat16")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+        raise ValueError("seqlens must be a contiguous int32 tensor of length batch")
+    _shape(out, (B, Hq, d), "out")
+    _dtype_code(out.dtype)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq)):
+        raise ValueError(f"lse must be a contiguous float32 [{B}, {Hq}] tensor")
+    _on_gpu(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens), ("out", out), ("lse", lse))
+    lib = load()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                               out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                               B, Hq, Hkv, Lmax, d, _strides3(k_cache), _dtype_code(out.dtype), float(scale),
+                               int(split_tokens), _stream(q.device))
+    _check(st)
+    return out, lse
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  seqlens: torch.Tensor, scale: float | None = None, split_tokens: int = 0,

@@ -451,8 +451,8 @@ size_t fa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_k
 
 namespace {
 
-// Argument checks of fa_decode (everything but the workspace), run before
-// anything touches the GPU.
+// Argument checks shared by fa_decode and fa_decode_noalloc (everything but
+// the workspace), run before anything touches the GPU.
 fa_status_t decode_checks(const char* fn, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* seqlens_k, const void* o, int32_t batch, int32_t heads_q,
                           int32_t heads_kv, int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
@@ -525,6 +525,27 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   return decode_launch("fa_decode", q, k_cache, v_cache, seqlens_k, o, lse, batch, heads_q, heads_kv, max_seqlen_k,
                        head_dim, kv_stride, out_dtype, softmax_scale, split_tokens, workspace, stream);
+}
+
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seqlens_k, void* o, float* lse,
+                              int32_t batch, int32_t heads_q, int32_t heads_kv,
+                              int32_t max_seqlen_k, int32_t head_dim, const int64_t kv_stride[3],
+                              fa_dtype_t out_dtype, float softmax_scale, int32_t split_tokens, void* stream) {
+  const fa_status_t st = decode_checks("fa_decode_noalloc", q, k_cache, v_cache, seqlens_k, o, batch, heads_q,
+                                       heads_kv, max_seqlen_k, head_dim, kv_stride, out_dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_bytes(batch, heads_q, heads_kv, max_seqlen_k, head_dim, split_tokens);
+  if (need > fa::kDecodeScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_decode_noalloc: these sizes need %zu bytes of partials, more than the %zu-byte static scratch "
+                "(use fa_decode with a workspace)", need, fa::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = fa::decode_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "fa_decode_noalloc: static scratch lookup failed: %s", hipGetErrorString(e));
+  return decode_launch("fa_decode_noalloc", q, k_cache, v_cache, seqlens_k, o, lse, batch, heads_q, heads_kv,
+                       max_seqlen_k, head_dim, kv_stride, out_dtype, softmax_scale, split_tokens, scratch, stream);
 }
 
 }  // extern "C"

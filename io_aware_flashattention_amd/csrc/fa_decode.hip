@@ -36,6 +36,8 @@
 // scalar loads one block ahead of the DMA that needs them, so the lookup never
 // waits on the vector-memory counter the DMA ring is paced by, and each lane
 // picks its row's page and slot with a compare, not a division.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -562,6 +564,33 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int decode_waves() { return 256 * FA_DEC_WPC; }
+
+// Static workspace of fa_decode_noalloc: the split kernel's partials live in
+// this file-scope device array instead of a caller's buffer. Every GPU the
+// library runs on holds its own copy (at its own address) until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device
+// memory: the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is passed on.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<uintptr_t> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  uintptr_t a = addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    a = reinterpret_cast<uintptr_t>(p);
+    addr[dev].store(a, std::memory_order_release);     // a racing first call stores the same address
+  }
+  *ptr = reinterpret_cast<void*>(a);
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.head_dim == 64) return p.out_fp32 ? launch_t<64, float>(p, stream) : launch_t<64, __bf16>(p, stream);

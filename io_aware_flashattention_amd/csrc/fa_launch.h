@@ -128,4 +128,9 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 int decode_waves();
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Size of the static decode workspace behind fa_decode_noalloc, and its
+// device address on the current device (looked up on the first call there).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

@@ -300,3 +300,36 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(FileNotFoundError):
         _lib.load()
+
+
+def _dec_noalloc(**kw):
+    lib = _lib.load()
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lens=FAKE + 0x300000, o=FAKE + 0x400000, lse=None,
+             B=2, Hq=16, Hkv=2, L=4096, d=128, kvs=(2 * 4096 * 128, 4096 * 128, 128), outd=0, scale=0.0884,
+             split=0)
+    a.update(kw)
+    kvs = (ctypes.c_int64 * 3)(*a["kvs"]) if a["kvs"] is not None else None
+    st = lib.fa_decode_noalloc(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                               a["L"], a["d"], kvs, a["outd"], a["scale"], a["split"], None)
+    return st, lib.fa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lens=None), 1, "non-null"),
+    (dict(B=0), 1, "positive"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(Hq=66, Hkv=1), 2, "at most 32"),
+    (dict(k=FAKE + 4), 2, "aligned"),
+    (dict(B=4096, Hq=64, Hkv=8), 2, "static scratch"),      # partials past the 16 MiB scratch
+])
+def test_decode_noalloc_rejects_before_launch(kw, status, needle):
+    st, msg = _dec_noalloc(**kw)
+    assert st == status, msg
+    assert needle in msg
+    assert "fa_decode_noalloc" in msg
+
+
+def test_decode_noalloc_limit_is_the_scratch_size():
+    lib = _lib.load()
+    assert lib.fa_decode_workspace_bytes(64, 64, 8, 32768, 128, 0) <= _lib.DECODE_SCRATCH_BYTES
+    assert lib.fa_decode_workspace_bytes(4096, 64, 8, 1024, 128, 0) > _lib.DECODE_SCRATCH_BYTES

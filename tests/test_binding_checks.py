@@ -77,6 +77,9 @@ def test_decode_refuses(kw, needle):
     a.update(kw)
     with pytest.raises(ValueError, match=needle):
         fa.decode(a["q"], a["k"], a["v"], a["lens"], out=a.get("out"))
+    if "out" not in kw:
+        with pytest.raises(ValueError, match=needle):
+            fa.decode_noalloc(a["q"], a["k"], a["v"], a["lens"], t(2, 16, 128))
 
 
 @pytest.mark.parametrize("kw,needle", [
