@@ -7,15 +7,20 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. split-KV decode, 64 sequences, 64 query heads over 8 kv heads, d = 128,
      kv lengths uniform in [1024, 32768], bf16 cache (fa_decode: split kernel
      and merge kernel).
-After the timed steps, five more paths are timed on their own (not part of
-the step): the same decode against a paged cache (fa_decode_paged: 16-token
+After the timed steps, more paths are timed on their own (not part of the
+step): the same decode against a paged cache (fa_decode_paged: 16-token
 pages in a token-major pool, shuffled block table) as ``decode_paged``, and
 through fa_fwd_varlen the 8192-token sliding-window-1024 prefill
 (``prefill_window``) and a packed batch of 16 causal sequences of 1..8192
 tokens (``prefill_varlen``), and the backward of the step's prefill through
 fa_bwd (``backward``, 2.5x the forward FLOPs), and the FP8 prefill of the
 step's workload (``prefill_fp8``: fa_fwd_fp8, with fa_fp8_quantize timed
-apart).
+apart). Then every other prefill configuration (``configs``: the fp32 single
+head, GPT-2-shaped causal prefill, the mid-length prefill causal and
+unmasked, and the 16384-token GQA prefill), each with its own algorithmic
+TFLOP/s, fraction of peak, HBM counter bytes when the committed counter
+summary matches the kernel sources, and the fp64 oracle timed on a bounded
+sample of the same configuration.
 Inputs are generated and uploaded before the timed region. W untimed warmup
 steps, then exactly K timed steps between two device synchronisations. Kernel
 durations come from HIP events recorded on the stream the kernels run on.
@@ -54,8 +59,13 @@ PREFILL_CFG = "c4a_gqa_8k"
 DECODE_CFG = "c5_decode"
 PAGE_SIZE = 16                # tokens per page of the paged-decode measurement
 PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.json")
-KERNEL_SOURCES = ["io_aware_flashattention_amd/csrc/fa_fwd.hip", "io_aware_flashattention_amd/csrc/fa_decode.hip",
-                  "io_aware_flashattention_amd/csrc/fa_device.h"]
+KERNEL_SOURCES = ["io_aware_flashattention_amd/csrc/" + f for f in
+                  ("fa_fwd.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_device.h",
+                   "fa_launch.h")]
+# prefill configurations timed after the step, in launch order (labels of the profile summaries)
+CONFIG_PHASES = ("c1_single_head_fp32", "c2_gpt2_causal", "c3_mid_causal", "c3_mid_none", "c4b_gqa_16k")
+ORACLE_SECONDS = {"c1_single_head_fp32": 1.0, "c2_gpt2_causal": 2.0, "c3_mid_causal": 3.0, "c3_mid_none": 3.0,
+                  "c4b_gqa_16k": 6.0, "c5_decode": 2.0}
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -228,6 +238,8 @@ def run(args):
                          "kernel": "fa_bwd (pre-pass + dK/dV + dQ)"}
     del dout, gq, gk, gv, bws
 
+    configs = config_phases(args, fa, W, cm, to_dev, time_launches, dev)
+
     pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
     kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -238,7 +250,9 @@ def run(args):
     pag_gbs = kv_bytes / (pag_avg * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / args.steps
 
-    traffic, traffic_dec = load_traffic()
+    traffic, traffic_dec, per_phase = load_traffic()
+    for name, c in configs.items():
+        c["traffic"] = per_phase.get(f"prefill {name}") if per_phase else None
     result = {
         "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
         "value": round(pre_tflops, 2),
@@ -274,11 +288,121 @@ def run(args):
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_dec,
                             "kernel": "fa_decode (split + merge)"},
         **extra,
+        "configs": configs,
         "kernel_sources": sources_hash(),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pc, args.cpu_seconds)
+        result["cpu_baseline"]["host"] = host_info()
+        for name, c in configs.items():
+            c["oracle"] = oracle_timing(W.CONFIGS[name], ORACLE_SECONDS[name], c["ms"])
+        result["decode_value"]["oracle"] = oracle_decode_timing(dc, lens, ORACLE_SECONDS["c5_decode"], dec_avg)
+        result["cpu_baseline"]["oracle_per_config"] = {n: c["oracle"] for n, c in configs.items()}
+        result["cpu_baseline"]["oracle_per_config"][DECODE_CFG] = result["decode_value"]["oracle"]
     print(json.dumps(result), flush=True)
+
+
+def config_phases(args, fa, W, cm, to_dev, time_launches, dev):
+    """Every other prefill configuration, timed on its own with HIP events:
+    algorithmic TFLOP/s (4 B Hq N^2 d, halved for causal), fraction of the bf16
+    peak. The fp32 single head is launch-bound (its bar is parity)."""
+    import numpy as np
+    import torch
+    out = {}
+    for name in CONFIG_PHASES:
+        c = W.CONFIGS[name]
+        t0 = time.time()
+        qh, kh, vh = W.make_prefill_inputs(c)
+        up = (lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)) if c.dtype == "fp32" else to_dev
+        q, k, v = up(qh), up(kh), up(vh)
+        del qh, kh, vh
+        o = torch.empty(q.shape, dtype=torch.bfloat16 if c.dtype == "bf16" else torch.float32, device=dev)
+        lse = torch.empty(c.batch, c.heads_q, c.seqlen, dtype=torch.float32, device=dev)
+        ms = time_launches(lambda: fa.fwd(q, k, v, causal=c.causal, scale=c.scale, out=o, lse=lse))
+        fl = cm.attention_flops(c.batch, c.heads_q, c.seqlen, c.seqlen, c.head_dim, c.causal)
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_launch": fl,
+                     "workload": f"B{c.batch} Hq{c.heads_q} Hkv{c.heads_kv} N{c.seqlen} d{c.head_dim} "
+                                 f"{'causal' if c.causal else 'no mask'}, {c.dtype} in, {o.dtype} out".replace(
+                                     "torch.", ""),
+                     "kernel": "fa_fwd"}
+        print(f"[bench] {name}: {ms:.4f} ms, {tf:.1f} TFLOP/s ({time.time() - t0:.1f}s with input generation)",
+              file=sys.stderr, flush=True)
+        del q, k, v, o, lse
+    return out
+
+
+def host_info():
+    """CPU model, core counts and NumPy's BLAS build of the host the oracle ran on."""
+    import numpy as np
+    import threadpoolctl
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "architecture")}
+            for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas}
+
+
+def oracle_timing(c, seconds: float, gpu_ms: float):
+    """The fp64 oracle on whole query heads of a prefill configuration (spread
+    over the kv groups) until about ``seconds`` of work: seconds per head,
+    executed fp64 GFLOP/s (the oracle materialises every score, so 4 Nq Nk d
+    per head even under the causal mask), the whole configuration's projected
+    oracle time and the GPU's speedup over it (context only)."""
+    from io_aware_flashattention_amd import workloads as W
+    from oracle import attention_ref
+    heads, elapsed = [], 0.0
+    units = [(b, h) for h in [(9 * i) % c.heads_q for i in range(c.heads_q)] for b in range(c.batch)]
+    for b, h in units:
+        kvh = h // c.group
+        q = W.to_f64(W.prefill_slice(c, "q", b, h))[None, None]
+        k = W.to_f64(W.prefill_slice(c, "k", b, kvh))[None, None]
+        v = W.to_f64(W.prefill_slice(c, "v", b, kvh))[None, None]
+        ts = time.perf_counter()
+        attention_ref(q, k, v, c.scale, causal=c.causal)
+        elapsed += time.perf_counter() - ts
+        heads.append((b, h))
+        if elapsed >= seconds:
+            break
+    per_head = elapsed / len(heads)
+    whole = per_head * c.batch * c.heads_q
+    return {"heads_timed": len(heads), "seconds": round(elapsed, 3), "seconds_per_head": round(per_head, 4),
+            "executed_fp64_gflops": round(4.0 * c.seqlen * c.seqlen * c.head_dim * len(heads) / elapsed / 1e9, 2),
+            "projected_config_seconds": round(whole, 2), "gpu_speedup": round(whole / (gpu_ms * 1e-3), 1)}
+
+
+def oracle_decode_timing(dc, lens, seconds: float, gpu_ms: float):
+    """The fp64 oracle on whole sequences of the decode workload until about
+    ``seconds`` of work, projected to all sequences."""
+    import numpy as np
+
+    from io_aware_flashattention_amd import workloads as W
+    from oracle import decode_ref
+    done, toks, elapsed = 0, 0, 0.0
+    for b in range(dc.batch):
+        n = int(lens[b])
+        q = W.to_f64(W.decode_query(dc, b))[None]
+        k = np.stack([W.to_f64(W.decode_kv_slice(dc, "k", b, h, n)) for h in range(dc.heads_kv)])[None]
+        v = np.stack([W.to_f64(W.decode_kv_slice(dc, "v", b, h, n)) for h in range(dc.heads_kv)])[None]
+        ts = time.perf_counter()
+        decode_ref(q, k, v, np.array([n]), dc.scale)
+        elapsed += time.perf_counter() - ts
+        done += 1
+        toks += n
+        if elapsed >= seconds:
+            break
+    whole = elapsed * float(lens.sum()) / toks
+    return {"sequences_timed": done, "seconds": round(elapsed, 3), "projected_config_seconds": round(whole, 2),
+            "gpu_speedup": round(whole / (gpu_ms * 1e-3), 1)}
 
 
 def load_traffic():
@@ -288,10 +412,11 @@ def load_traffic():
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        return None, None, None
     if d.get("kernel_sources") != sources_hash():
-        return None, None
-    return d.get("prefill_bytes_per_launch"), d.get("decode_bytes_per_launch")
+        return None, None, None
+    per = {k: v["fetch"] + v["write"] for k, v in d.get("per_phase_bytes", {}).items()}
+    return d.get("prefill_bytes_per_launch"), d.get("decode_bytes_per_launch"), per
 
 
 def cpu_baseline(pc, seconds: float):
@@ -341,11 +466,21 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
     (prefill, decode split, decode merge); n_launch paged decodes (paged split,
     merge); n_launch window prefills; n_launch packed prefills; the fp8
     quantiser and prefill (their own kernels); one prefill for the backward's
-    inputs, then n_launch backward passes. The prefill
-    kernel is the same instantiation in every prefill phase, so the phase
-    comes from the dispatch order."""
+    inputs, then n_launch backward passes; then n_launch prefills of each
+    configuration in CONFIG_PHASES. One prefill kernel serves several phases,
+    so the phase comes from the dispatch order."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     seen = {"fwd": 0, "merge": 0}
+    fwd_phases = [("prefill c4a (step)", n_launch), ("prefill window c7", n_launch),
+                  ("prefill varlen c6", n_launch), ("prefill c4a (backward inputs)", 1)]
+    fwd_phases += [(f"prefill {c}", n_launch) for c in CONFIG_PHASES]
+
+    def fwd_label(i):
+        for label, n in fwd_phases:
+            if i < n:
+                return label
+            i -= n
+        return None
     out = []
     for r in rows:
         name = r.get(name_key, "")
@@ -354,8 +489,7 @@ def _dispatch_labels(rows, name_key: str, n_launch: int):
         elif re.search(r"fwd_\w*kernel", name):
             i = seen["fwd"]
             seen["fwd"] += 1
-            label = ("prefill c4a (step)", "prefill window c7", "prefill varlen c6",
-                     "prefill c4a (backward inputs)")[min(3, i // n_launch)]
+            label = fwd_label(i)
         elif "bwd_" in name:
             label = "backward " + re.sub(r".*(bwd_\w+?_kernel).*", r"\1", name)
         elif "decode_split" in name:            # contiguous: template flag false (mangled "Lb0E")
@@ -464,6 +598,9 @@ def phase_flops():
     pre = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)
     out = {"prefill c4a (step)": pre, "prefill c4a (backward inputs)": pre, "fp8 fwd_fp8_kernel": pre,
            "backward (dK/dV + dQ)": cm.backward_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, True)}
+    for name in CONFIG_PHASES:
+        c = W.CONFIGS[name]
+        out[f"prefill {name}"] = cm.attention_flops(c.batch, c.heads_q, c.seqlen, c.seqlen, c.head_dim, c.causal)
     for label, name in (("prefill window c7", "c7_window_8k"), ("prefill varlen c6", "c6_varlen_causal")):
         vc = W.VARLEN_CONFIGS[name]
         vl = W.varlen_lengths(vc)

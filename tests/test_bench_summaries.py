@@ -24,6 +24,9 @@ BWD = [("void fa::detail::bwd_pre_kernel<128>(fa::BwdParams)", "backward bwd_pre
        ("_ZN2fa6detail15bwd_dkdv_kernelILi128ELb1EDF16bEEvNS_9BwdParamsE", "backward bwd_dkdv_kernel"),
        ("_ZN2fa6detail13bwd_dq_kernelILi128ELb1EDF16bEEvNS_9BwdParamsE", "backward bwd_dq_kernel")]
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>"
+F32 = "_ZN2fa6detail14fwd_f32_kernelILi64ELb0EfEEvNS_9FwdParamsE"
+FWD64 = "_ZN2fa6detail15fwd_bf16_kernelILi64ELb1EDF16bLi4ELi1ELi3EEEvNS_9FwdParamsE"
+FWD_NONE = "_ZN2fa6detail13fwd_pp_kernelILi128ELb0EDF16bLi3EEEvNS_9FwdParamsE"
 
 
 def bench_dispatches(n):
@@ -41,6 +44,8 @@ def bench_dispatches(n):
     seq += [(FWD, "prefill c4a (backward inputs)")]
     for _ in range(n):
         seq += BWD
+    for cfg, kern in zip(bench.CONFIG_PHASES, (F32, FWD64, FWD, FWD_NONE, FWD)):
+        seq += [(kern, f"prefill {cfg}")] * n
     return seq
 
 
