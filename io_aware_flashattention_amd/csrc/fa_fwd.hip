@@ -488,7 +488,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 // wave of each group per SIMD). A wave's work is a chain of units separated by
 // workgroup barriers:
 //   G(j): S_{j+1}^T = K_{j+1} Q^T and O^T += V_j^T P_j^T (matrix cores),
-//   S(j): mask, row maxima, exponentials and row sums of tile j (vector ALUs),
+//   S(j): mask, row maxima, exponentials and row sums of tile j (vector ALUs;
+//         the sum of the bf16 weights goes to the matrix core from here),
 // in the order G(-1) S(0) G(0) S(1) G(1) ... . Group 1 runs one unit behind
 // group 0, so in every phase between two barriers one wave of each SIMD feeds
 // the matrix core while the other runs the softmax, and the two swap at the
@@ -762,7 +763,7 @@ void fwd_pp_kernel(const FwdParams p) {
     }
   }
   // Sum of the bf16 weights that enter P V, on the matrix core (v_dot2c runs
-  // on the matrix pipe too, so it would stall the other group's MFMAs): a
+  // on the matrix pipe too, so it would stall the other wave's MFMAs): a
   // P^T chunk read as the B operand of v_mfma_f32_16x16x32_bf16 holds, in
   // column n, keys 0-7 and 8-15 of rows n and n+16; the A operand below is 1
   // where the key group belongs to the row this lane's accumulator holds
@@ -808,7 +809,6 @@ void fwd_pp_kernel(const FwdParams p) {
             (__attribute__((address_space(3))) bf16x4*)(va + 4 * D));
         o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[c], o[db]);
       }
-      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[c], lsum, 0, 0, 0);
     }
   };
   // Both halves of a G unit with the LDS fragment reads issued AHEAD steps
@@ -852,8 +852,6 @@ void fwd_pp_kernel(const FwdParams p) {
       read(KSTEPS + i + AHEAD);
       o[i % DBLK] = mfma32(__builtin_shufflevector(vf[i][0], vf[i][1], 0, 1, 2, 3, 4, 5, 6, 7), pb[i / DBLK],
                            o[i % DBLK]);
-      if (i % DBLK == DBLK - 1)
-        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[i / DBLK], lsum, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -905,6 +903,11 @@ void fwd_pp_kernel(const FwdParams p) {
     }
     const float rs = (rq[0] + rq[1]) + (rq[2] + rq[3]);
     l_run += half_swap_sum(rs);
+    // the bf16 weights' sum goes to the matrix core from the softmax unit, so
+    // that both waves of a SIMD feed it in this phase (the other one is in
+    // its matrix unit); same products, same order, same bits
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[c], lsum, 0, 0, 0);
   };
 
   // Phases are numbered within the current item: at phase 2t+4 (group 1) or
