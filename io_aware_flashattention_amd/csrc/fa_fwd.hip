@@ -118,22 +118,23 @@ __device__ __forceinline__ SeqView seq_view(const FwdParams& p, int b, int hq, i
   return s;
 }
 
-// Logical work item (batch, kv head, query tile, query head of the group;
-// head fastest) of hardware workgroup wg, or -1 for grid padding. Workgroups
+// Logical work item (batch, kv head, query tile, query head of the group, or
+// group of 2^hp_log2 of them; head fastest) of hardware workgroup wg, or -1
+// for grid padding. Workgroups
 // are dealt to the 8 XCDs round-robin (wg % 8), each XCD with its own L2.
 //   Dense batch: every (batch, kv head) row of query tiles costs the same, so
 //   each XCD takes a contiguous range of the logical order; its resident
 //   workgroups then share one kv head's K/V in its L2.
 //   Packed batch: rows cost what their sequence's length makes them cost, and
 //   contiguous ranges would leave some XCDs with long sequences and others
-//   idle. Chunks of G workgroups (the query heads that share a kv head and a
-//   query tile, kept on one XCD) are dealt to the XCDs in a snake order: 0..7,
+//   idle. Chunks of G >> hp_log2 workgroups (the query heads that share a kv
+//   head and a query tile, kept on one XCD) are dealt to the XCDs in a snake order: 0..7,
 //   7..0, 0..7, ... Along one row, XCD x then gets tiles x, 15-x, 16+x, 31-x,
 //   ..., whose causal costs pair up heavy with light, and the XCDs stay
 //   balanced whatever the length mix. The grid is padded to whole rounds.
 __device__ __forceinline__ int work_item(int wg, int n, const FwdParams& p) {
   if (p.cu_seqlens != nullptr) {
-    const int G = p.group;
+    const int G = p.group >> p.hp_log2;
     const int x = wg & 7, k = wg >> 3;
     const int r = k / G, g = k - r * G;
     const int j = (r & 1) ? 7 - x : x;
@@ -148,8 +149,9 @@ __device__ __forceinline__ int work_item(int wg, int n, const FwdParams& p) {
 // Grid for the logical work items of a launch.
 inline int64_t grid_for(const FwdParams& p) {
   if (p.cu_seqlens == nullptr) return p.n_items;
-  const int64_t chunks = p.n_items / p.group;
-  return (chunks + 7) / 8 * 8 * p.group;
+  const int G = p.group >> p.hp_log2;
+  const int64_t chunks = p.n_items / G;
+  return (chunks + 7) / 8 * 8 * G;
 }
 
 }  // namespace
@@ -495,6 +497,12 @@ void fwd_bf16_kernel(const FwdParams p) {
 // the matrix core while the other runs the softmax, and the two swap at the
 // next barrier.
 //
+// An item is 256 query rows of one head, or under the causal mask 256 / h
+// rows of h heads that share a kv head (h up to 8, a power of two dividing
+// the group): the waves' rows then span fewer keys, so fewer key tiles are
+// streamed that only some of the waves use (at the diagonal, and at a
+// window's far edge).
+//
 // A dense batch (or a packed batch of one sequence) runs on a persistent
 // grid: one workgroup per compute unit, each with a fixed list of work
 // items, and the K/V tiles of a workgroup's
@@ -511,7 +519,6 @@ template <int D, bool CAUSAL, typename TOut, int STAGES>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const FwdParams p) {
   constexpr int NW = 8;
-  constexpr int BRW = 32 * NW;               // query rows per item
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = BC * D;
@@ -548,7 +555,6 @@ void fwd_pp_kernel(const FwdParams p) {
     grp = __builtin_amdgcn_readfirstlane(tk) & 1;
     __syncthreads();
   }
-
   // Work items of this workgroup. Persistent grid (a dense batch, or a packed
   // batch of one sequence, whose items cost what a dense batch's do): the
   // workgroups of XCD x (blockIdx % 8,
@@ -556,7 +562,7 @@ void fwd_pp_kernel(const FwdParams p) {
   // order that work_item gives x, dealt out in a snake (round k left to right
   // for even k, right to left for odd k). Each (batch, kv head) row of the
   // logical order lists its query tiles heaviest first, with the query heads
-  // of a kv head side by side, so two consecutive rounds give the workgroups
+  // (or head groups) of a kv head side by side, so two consecutive rounds give the workgroups
   // nearly the same causal cost (the same when a row holds whole pairs of
   // rounds and a round whole groups of heads). A packed sequence's real
   // length (the caller's longest length may overstate it) sets its item count
@@ -569,14 +575,20 @@ void fwd_pp_kernel(const FwdParams p) {
     const const_i32* cu = (const const_i32*)p.cu_seqlens;
     const int s0 = min(max(cu[0], 0), p.total);
     const int s1 = min(max(cu[1], s0), p.total);
-    n_qt = (s1 - s0 + BRW - 1) / BRW;
-    n_items = p.heads_q * n_qt;
+    const int brw_l = 8 - p.hp_log2;
+    n_qt = (s1 - s0 + (1 << brw_l) - 1) >> brw_l;
+    n_items = (p.heads_q >> p.hp_log2) * n_qt;
     qt_s = n_qt <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n_qt - 1));
     qt_m = n_qt <= 1 ? 0u : (uint32_t)((((uint64_t)1 << (31 + qt_s)) + (uint64_t)n_qt - 1) / (uint64_t)n_qt);
   }
+  // An item is 256 >> hp_log2 query rows of 1 << hp_log2 query heads of one
+  // kv head: wave w takes head w >> rwl of them (rwl = 3 - hp_log2) and its
+  // rows 32 (w % 2^rwl) on. With several heads per item the waves' rows span
+  // fewer keys, so under the causal mask or a window fewer key tiles are
+  // loaded that only some of the waves use.
   struct Item {
-    int64_t q, k, v, o, lse;                 // element offsets of its (sequence, head)
-    int nq, nk, q0, jbase, ntiles;
+    int64_t q, k, v, o, lse;                 // element offsets of its sequence (q, o, lse: this wave's head)
+    int nq, nk, w0, jbase, ntiles;           // w0: this wave's first query row
     bool valid;
   };
   // (called once per item; its inputs pass through an empty asm statement so
@@ -590,8 +602,9 @@ void fwd_pp_kernel(const FwdParams p) {
   };
   auto make_item = [&](int idx) __attribute__((always_inline)) {
     Item it{};
-    int n = n_items, bid = blockIdx.x, nwg = gridDim.x, group = p.group, nqt = n_qt, hkv = p.heads_kv;
-    asm volatile("" : "+s"(n), "+s"(bid), "+s"(nwg), "+s"(group), "+s"(nqt), "+s"(hkv), "+s"(idx));
+    int n = n_items, bid = blockIdx.x, nwg = gridDim.x, nqt = n_qt, hkv = p.heads_kv, hpl = p.hp_log2, wu = wave_u;
+    asm volatile("" : "+s"(n), "+s"(bid), "+s"(nwg), "+s"(nqt), "+s"(hkv), "+s"(hpl), "+s"(wu), "+s"(idx));
+    const int group = p.group >> hpl, rwl = 3 - hpl;
     int L;
     if (persist) {
       const int per = n >> 3, rem = n & 7, x = bid & 7;
@@ -611,16 +624,17 @@ void fwd_pp_kernel(const FwdParams p) {
     L = d;
     const int b = rdiv(L, 2);
     const int kvh = L - b * hkv;
-    const int hq = kvh * group + g;
+    const int hq = kvh * p.group + (g << hpl) + (wu >> rwl);     // this wave's query head
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const SeqView sv = seq_view(p, b, hq, kvh);
-    it.q0 = qt * BRW;
-    if (it.q0 >= sv.nq) return it;           // a packed sequence shorter than the longest
+    const int q0 = qt << (5 + rwl);
+    if (q0 >= sv.nq) return it;              // a packed sequence shorter than the longest
+    it.w0 = q0 + 32 * (wu & ((1 << rwl) - 1));
     it.q = sv.q; it.k = sv.k; it.v = sv.v; it.o = sv.o; it.lse = sv.lse;
     it.nq = sv.nq; it.nk = sv.nk;
-    const int kv_end = CAUSAL ? min(it.nk, it.q0 + BRW) : it.nk;
+    const int kv_end = CAUSAL ? min(it.nk, q0 + (32 << rwl)) : it.nk;
     // tiles wholly behind every row's window are never loaded
-    it.jbase = (CAUSAL && p.window >= 0) ? max(0, it.q0 - p.window) / BC : 0;
+    it.jbase = (CAUSAL && p.window >= 0) ? max(0, q0 - p.window) / BC : 0;
     it.ntiles = (kv_end + BC - 1) / BC - it.jbase;
     it.valid = true;
     return it;
@@ -629,7 +643,7 @@ void fwd_pp_kernel(const FwdParams p) {
   const Item it0 = make_item(0);
   if (!it0.valid) return;                    // whole workgroup
   // the current item (its first K/V tile is stream tile c_t0)
-  int c_t0 = 0, c_nt = it0.ntiles, c_nk = it0.nk, c_jb = it0.jbase, c_q0 = it0.q0, c_nq = it0.nq;
+  int c_t0 = 0, c_nt = it0.ntiles, c_nk = it0.nk, c_jb = it0.jbase, c_w0 = it0.w0, c_nq = it0.nq;
   int64_t c_o = it0.o, c_lse = it0.lse;
 
   const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q);
@@ -679,7 +693,7 @@ void fwd_pp_kernel(const FwdParams p) {
   const char* ik = reinterpret_cast<const char*>(kg + it0.k + (int64_t)it0.jbase * BC * ks2);
   const char* iv = reinterpret_cast<const char*>(vg + it0.v + (int64_t)it0.jbase * BC * vs2);
   int irem = it0.nk - it0.jbase * BC;
-  issue_q(qg + it0.q + (int64_t)(it0.q0 + 32 * wave_u) * qs2, it0.nq - it0.q0 - 32 * wave_u);
+  issue_q(qg + it0.q + (int64_t)it0.w0 * qs2, it0.nq - it0.w0);
   // the next item (read once per item: these may live in spill lanes)
   Item nx;
   const char* nx_k;
@@ -944,8 +958,8 @@ void fwd_pp_kernel(const FwdParams p) {
     nx_k = reinterpret_cast<const char*>(kg + nx.k + (int64_t)nx.jbase * BC * ks2);
     nx_v = reinterpret_cast<const char*>(vg + nx.v + (int64_t)nx.jbase * BC * vs2);
     nx_rem = nx.nk - nx.jbase * BC;
-    nx_q = qg + nx.q + (int64_t)(nx.q0 + 32 * wave_u) * qs2;
-    nx_qr = nx.nq - nx.q0 - 32 * wave_u;
+    nx_q = qg + nx.q + (int64_t)nx.w0 * qs2;
+    nx_qr = nx.nq - nx.w0;
 
     // Item start: its first tiles (and query rows) are issued, mostly during
     // the previous item already. The query rows are read before the stream
@@ -965,12 +979,15 @@ void fwd_pp_kernel(const FwdParams p) {
     issue_upto(c_t0 + STAGES - 1);
     barrier();
 
-    wrow0 = c_q0 + wave * 32;
+    wrow0 = c_w0;
+    asm volatile("" : "+v"(wrow0));
     row = wrow0 + r32;
     // Tiles this wave needs: [lo_w, nt_w). Without the mask that is every
-    // tile, but the bound is still written in terms of the wave's rows (equal
-    // to ntiles since wrow0 >= 0): a wave-uniform bound lets the compiler turn
-    // the unit loop into uniform branches whose register allocation spills.
+    // tile, but the bound is still written in terms of the wave's first row
+    // (equal to ntiles since wrow0 >= 0), and that row sits in a vector
+    // register, a per-lane value to the compiler: a wave-uniform bound lets
+    // it turn the unit loop into uniform branches whose register allocation
+    // spills.
     nt_w = CAUSAL ? min(c_nt, (wrow0 + 31) / BC + 1 - c_jb)
                   : min(c_nt, (wrow0 + c_nk + BC - 1) / BC);
     lo_w = W >= 0 ? max(0, wrow0 - W) / BC - c_jb : 0;
@@ -1064,7 +1081,7 @@ void fwd_pp_kernel(const FwdParams p) {
     issue_upto(c_t0 + c_nt);                          // the next item's first tile (normally issued already)
     ++idx;
     c_t0 += c_nt;
-    c_nt = nx.ntiles; c_nk = nx.nk; c_jb = nx.jbase; c_q0 = nx.q0; c_nq = nx.nq;
+    c_nt = nx.ntiles; c_nk = nx.nk; c_jb = nx.jbase; c_w0 = nx.w0; c_nq = nx.nq;
     c_o = nx.o; c_lse = nx.lse;
   }
 }
@@ -1104,9 +1121,17 @@ inline int device_cus() {
 template <int D, bool CAUSAL, typename TOut, int STAGES>
 hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
-  q.n_qtiles = (p.seqlen_q + 255) / 256;
-  q.n_items = q.batch * q.heads_q * q.n_qtiles;
-  fa_reciprocal(q.group, &q.div_m[0], &q.div_s[0]);
+  // Under the causal mask (and a window) an item takes up to 8 query heads of
+  // a kv head with 256 / 8 rows each: all its waves then need the same key
+  // tiles, where 256 rows of one head span 4 more tiles at the diagonal (and
+  // 4 more at a window's far edge) that only some of the waves use.
+  q.hp_log2 = 0;
+  if (CAUSAL)
+    while (q.hp_log2 < 3 && q.group % (2 << q.hp_log2) == 0) ++q.hp_log2;
+  const int brw = 256 >> q.hp_log2;
+  q.n_qtiles = (p.seqlen_q + brw - 1) / brw;
+  q.n_items = q.batch * (q.heads_q >> q.hp_log2) * q.n_qtiles;
+  fa_reciprocal(q.group >> q.hp_log2, &q.div_m[0], &q.div_s[0]);
   fa_reciprocal(q.n_qtiles, &q.div_m[1], &q.div_s[1]);
   fa_reciprocal(q.heads_kv, &q.div_m[2], &q.div_s[2]);
   // persistent (dense, or packed with one sequence): one workgroup per

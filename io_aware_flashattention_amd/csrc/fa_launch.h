@@ -16,7 +16,7 @@ struct FwdParams {
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
   int batch, heads_q, heads_kv, group, seqlen_q, seqlen_k, head_dim;
   int n_qtiles;
-  int n_items;       // batch * heads_q * n_qtiles logical workgroups
+  int n_items;       // batch * (heads_q >> hp_log2) * n_qtiles logical work items
   float scale_log2;  // softmax scale * log2(e)
   bool causal, in_fp32, out_fp32;
   // Packed batch (null: dense): sequence b owns tokens cu_seqlens[b] ..
@@ -33,6 +33,9 @@ struct FwdParams {
   uint32_t div_m[3];
   int div_s[3];
   bool persist;      // d = 128 kernel: a persistent grid walks the items (set by its launcher)
+  // d = 128 kernel: an item is 256 >> hp_log2 query rows of 1 << hp_log2 query
+  // heads that share a kv head (set by its launcher; 0 elsewhere)
+  int hp_log2;
 };
 
 // The reciprocal (m, s) of d >= 1 described at FwdParams::div_m. With
