@@ -252,8 +252,25 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   const bool causal = p.causal;
   const int n = p.seqlen, npad = (n + KT - 1) / KT * KT;
   const int nqt = (n + BRW - 1) / BRW;
-  const int t = blockIdx.x % nqt;
-  const int bh = blockIdx.x / nqt;
+  // Causal: in dispatch order every head's heaviest query tile first, then
+  // every head's next one, so long workgroups start first and short ones
+  // fill in behind them. When the kv groups come in whole rounds of 8, the
+  // heads of one kv group go to one XCD (workgroups are dealt to the 8 XCDs
+  // round-robin) and share its L2.
+  int t, bh;
+  if (causal) {
+    const int nh = p.batch * p.heads_q, nkv = p.batch * p.heads_kv;
+    t = blockIdx.x / nh;
+    bh = blockIdx.x - t * nh;
+    if (nkv % 8 == 0) {
+      const int x = bh & 7, sl = bh >> 3;
+      const int kg = x + 8 * (sl / p.group);
+      bh = kg * p.group + sl % p.group;
+    }
+  } else {
+    t = blockIdx.x % nqt;
+    bh = blockIdx.x / nqt;
+  }
   const int hq = bh % p.heads_q, b = bh / p.heads_q;
   const int kvh = hq / p.group;
   const int qt = causal ? nqt - 1 - t : t;   // heavy tiles first
@@ -332,19 +349,25 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   // S^T tile = K Q^T for the 64 keys of a tile: block blk holds keys 32 blk .. +31
   auto scores = [&](int tile, f32x16 (&s)[2]) {
     const uint8_t* ks_ = smem + (tile % ST8) * 2 * TILEB;
+    // all four A fragments are read first, and the two accumulation chains
+    // alternate, so no product waits for the one before it
+    i32x8 af[2][2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      const int kr = 32 * blk + r32;         // key row of this lane's A fragment
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int blk = 0; blk < 2; ++blk) {
+        const int kr = 32 * blk + r32;       // key row of this lane's A fragment
         const int c0 = 4 * ks + 2 * half;
         const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * (c0 ^ ((kr >> 1) & 7)));
         const u32x4 c = *reinterpret_cast<const u32x4*>(ks_ + kr * D8 + 16 * ((c0 + 1) ^ ((kr >> 1) & 7)));
-        const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-        s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf[ks], s[blk], 0, 0, 0, 127, 0, 127);
+        af[ks][blk] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
       }
-    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][blk], qf[0], f32x16{}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][blk], qf[1], s[blk], 0, 0, 0, 127, 0, 127);
   };
   // every wave has waited for its own loads of tiles j and j+1; the barrier
   // publishes them and frees the stage of tile j-1 (its K was read two steps
