@@ -4,9 +4,10 @@ Small and ragged shapes are checked element by element in full, and so is
 the long-context GQA workload at 8192 tokens (all 524,288 rows). The others
 are checked in full where the oracle finishes in seconds and otherwise on
 sampled rows of every head: first, last, tile-boundary and heavy-key rows,
-and at least one row of every 256-row work item (the persistent kernel
-streams K/V tiles and query rows across items, so a fault tied to one ring
-position would show only on the rows of the items it hits).
+and at least one row of every 32-row block of every head, so of every work
+item (the persistent kernel streams K/V tiles and query rows across items,
+so a fault tied to one ring position would show only on the rows of the
+items it hits).
 """
 import numpy as np
 import pytest
@@ -107,9 +108,12 @@ def test_c2_gpt2_causal():
 
 
 def _per_item_rows(n, seed):
-    """One row inside every 256-row work item, at a seeded offset."""
-    rng = np.random.default_rng([seed, 256])
-    return {min(n - 1, i + int(rng.integers(0, 256))) for i in range(0, n, 256)}
+    """One row inside every 32-row block, at a seeded offset: a work item
+    holds 256 rows of one head, or under the causal mask 256 / h rows of h
+    heads that share a kv head (h up to 8), so every item of every head is
+    sampled."""
+    rng = np.random.default_rng([seed, 32])
+    return {min(n - 1, i + int(rng.integers(0, 32))) for i in range(0, n, 32)}
 
 
 def _sample_rows(n, seed, extra=()):
@@ -169,16 +173,18 @@ def test_persistent_items_with_ragged_tiles(B, causal):
 
 
 # (B, Hq, Hkv, N, causal): 1 to 5 items per workgroup of the persistent grid,
-# kv groups of 1, 2 and 8, ragged and whole last key tiles
+# kv groups of 1, 2, 4, 8 and 16 (under the causal mask: items of 1, 2, 4 and
+# 8 heads, and two 8-head items per kv head), ragged and whole last key tiles
 SWEEP = [(1, 128, 128, 700, True), (2, 96, 48, 517, False), (4, 64, 8, 384, True), (1, 256, 32, 1100, True),
-         (3, 40, 5, 830, False), (2, 160, 20, 960, True)]
+         (3, 40, 5, 830, False), (2, 160, 20, 960, True), (2, 32, 16, 900, True), (1, 64, 16, 777, True),
+         (1, 64, 4, 1000, True)]
 
 
 @pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n"))
 def test_persistent_shape_sweep(shape):
     """Seeded shapes whose item counts give the persistent workgroups one to
     five items each; sampled rows of every head (edges, tile boundaries, a
-    head-dependent row, and one row inside every 256-row work item)."""
+    head-dependent row, and one row inside every 32-row block)."""
     B, Hq, Hkv, N, causal = shape
     q, k, v = W.make_random_prefill(B, Hq, Hkv, N, N, 128, seed=900 + N, heavy_frac=0.02)
     edges = [0, 1, 63, 64, 255, 256, N // 2, N - 65, N - 64, N - 2, N - 1]
