@@ -30,9 +30,13 @@ TFLOP/s (4*B*Hq*N^2*d, halved for the causal mask); the decode bandwidth in
 algorithmic KV GB/s (every cached K/V byte of every valid token, read once)
 is reported alongside. ``roofline`` / ``roofline_decode`` put both against
 MI355X peaks; ``cpu_baseline`` times the fp64 oracle on a sample of the same
-prefill workload on the host cores.
+prefill workload on the host cores. ``clock`` records the shader clock the
+chip ran at under the prefill (read from the SMU after the timed regions;
+clocks are not pinned) and the prefill's fraction of the matrix peak at that
+clock, beside the fraction of the published 2.4 GHz peak that ``roofline``
+reports.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-clock]
     python bench.py --summarize-trace DIR --out FILE [--steps K --warmup W]   (rocprofv3 kernel trace -> text)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE [--steps K --warmup W]  (HBM bytes per launch)
   (--steps/--warmup: those of the profiled run, so its dispatches can be split into the bench's phases)
@@ -55,6 +59,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 matrix peak (twice bf16)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PEAK_CLOCK_MHZ = 2400.0       # the shader clock the published matrix peaks assume
 PREFILL_CFG = "c4a_gqa_8k"
 DECODE_CFG = "c5_decode"
 PAGE_SIZE = 16                # tokens per page of the paged-decode measurement
@@ -239,6 +244,8 @@ def run(args):
     del dout, gq, gk, gv, bws
 
     configs = config_phases(args, fa, W, cm, to_dev, time_launches, dev)
+    clock = None if args.no_clock else observed_clock(
+        lambda: fa.fwd(q, k, v, causal=True, scale=pc.scale, out=o, lse=lse), sum(pre_ms) / len(pre_ms))
 
     pre_flops = cm.attention_flops(pc.batch, pc.heads_q, pc.seqlen, pc.seqlen, pc.head_dim, causal=True)
     kv_bytes = cm.decode_kv_bytes(lens, dc.heads_kv, dc.head_dim)
@@ -291,6 +298,12 @@ def run(args):
         "configs": configs,
         "kernel_sources": sources_hash(),
     }
+    if clock is not None:
+        if clock.get("mhz_mean"):
+            peak_clk = PEAK_BF16_TFLOPS * clock["mhz_mean"] / PEAK_CLOCK_MHZ
+            clock["bf16_peak_at_this_clock"] = round(peak_clk, 1)
+            clock["prefill_frac_at_this_clock"] = round(pre_tflops / peak_clk, 4)
+        result["clock"] = clock
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pc, args.cpu_seconds)
         result["cpu_baseline"]["host"] = host_info()
@@ -300,6 +313,59 @@ def run(args):
         result["cpu_baseline"]["oracle_per_config"] = {n: c["oracle"] for n, c in configs.items()}
         result["cpu_baseline"]["oracle_per_config"][DECODE_CFG] = result["decode_value"]["oracle"]
     print(json.dumps(result), flush=True)
+
+
+def observed_clock(launch, launch_ms: float, seconds: float = 2.5, settle: float = 1.5):
+    """The shader (GFX) clock the chip runs at under the prefill: `launch` runs
+    back to back for `seconds`, and after `settle` seconds of that load the
+    per-XCD current clocks are read from the SMU metrics (amdsmi), which
+    refresh about once a second with roughly one-second averages. The bench
+    does not pin clocks; this records what it observed. It runs after every
+    timed region, so it perturbs none of them."""
+    import torch
+    try:
+        import amdsmi
+    except Exception as e:                   # noqa: BLE001 - reported, not fatal
+        return {"source": None, "error": f"amdsmi not importable: {e}"}
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as e:                   # noqa: BLE001
+        return {"source": None, "error": f"amdsmi_init failed: {e}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return {"source": None, "error": f"{len(handles)} GPUs visible to amdsmi; the bench's one is ambiguous"}
+        chunk = max(1, int(100.0 / max(launch_ms, 1e-3)))       # about 0.1 s of GPU work
+        t0 = time.time()
+        reads = []
+        while time.time() - t0 < seconds:
+            for _ in range(chunk):
+                launch()
+            torch.cuda.synchronize()
+            if time.time() - t0 >= settle:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handles[0])
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 65535]
+                if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+                    clks = [m["current_gfxclk"]]
+                if clks:
+                    reads.append(clks)
+        if not reads:
+            return {"source": None, "error": "no current GFX clock in the SMU metrics"}
+        k = len(reads[-1])
+        rows = [r for r in reads if len(r) == k]
+        mean_x = [round(sum(r[i] for r in rows) / len(rows), 1) for i in range(k)]
+        return {"source": "amdsmi GPU metrics, current_gfxclks (per XCD, ~1 s averages)",
+                "under": f"fa_fwd c4a back to back for {seconds:g} s, read after {settle:g} s",
+                "reads": len(rows), "mhz_per_xcd": mean_x, "mhz_mean": round(sum(mean_x) / len(mean_x), 1),
+                "peak_assumes_mhz": PEAK_CLOCK_MHZ}
+    except Exception as e:                   # noqa: BLE001
+        torch.cuda.synchronize()
+        return {"source": None, "error": f"amdsmi query failed: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:                    # noqa: BLE001
+            pass
 
 
 def config_phases(args, fa, W, cm, to_dev, time_launches, dev):
@@ -663,6 +729,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock after the timed regions")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-mops", metavar="DIR")
