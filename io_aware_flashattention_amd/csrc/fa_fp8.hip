@@ -380,7 +380,7 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     if (j + ST8 - 1 < ntiles) issue(j + ST8 - 1, (j + ST8 - 1) % ST8);
   };
-  auto softmax_pv = [&](auto edge_c, int j, f32x16 (&sc)[2]) {
+  auto softmax_pv = [&](auto edge_c, int j, f32x16 (&sc)[2], float ce) {
     constexpr bool EDGE = decltype(edge_c)::value;   // the tile holds masked keys
     const uint8_t* vs_ = smem + (j % ST8) * 2 * TILEB + TILEB;
     const int kv0 = j * KT;
@@ -389,7 +389,6 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     // and one FMA per score both scales and subtracts the base; the base is
     // lowered by 8 so the weights come out as 2^8 * 2^(x - m), ready for e4m3.
     l8 += ls[0];                             // the previous tile's weights, at the current base
-    const float ce = c2 * ksc[j];
     // a key is visible when key <= lim; relative to this lane's first key of the tile
     const int rel = (causal ? min(row, n - 1) : n - 1) - kv0 - 4 * half;
     float x[2][16];
@@ -447,15 +446,25 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   scores(0, sa);                             // every wave has at least one tile
+  // the key scale of tile j is read one step ahead, so its scalar load is
+  // not waited for at the start of the tile's softmax
+  float ks_cur = ksc[0], ks_nxt = 0.f;
   auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     sync_tile(j);
     if (j + 1 < nt_w) scores(j + 1, nxt);
+    // this tile's scale (its load landed a step ago) is taken before the next
+    // one is requested: scalar loads return out of order, so a wait for one
+    // is a wait for all
+    float ce = c2 * ks_cur;
+    asm volatile("" : "+v"(ce));
     __builtin_amdgcn_sched_barrier(0);
+    ks_nxt = ksc[min(j + 1, ntiles - 1)];   // lands during the softmax
     if (j < nt_w) {                          // later tiles are wholly in this wave's future
       const int kv0 = j * KT;
-      if ((causal && kv0 + KT - 1 > wrow0) || kv0 + KT > n) softmax_pv(bool_c<true>{}, j, cur);
-      else softmax_pv(bool_c<false>{}, j, cur);
+      if ((causal && kv0 + KT - 1 > wrow0) || kv0 + KT > n) softmax_pv(bool_c<true>{}, j, cur, ce);
+      else softmax_pv(bool_c<false>{}, j, cur, ce);
     }
+    ks_cur = ks_nxt;
   };
   for (int j = 0; j < ntiles; j += 2) {
     step(j, sa, sb);
