@@ -956,7 +956,6 @@ void fwd_pp_kernel(const FwdParams p) {
   // ev_ph: this wave's next refill phase; permit: the last stream tile whose
   // stage is free by then
   int ev_ph, permit;
-  bool ready = false;                        // the current item's first tile and query rows have landed
   auto phase_begin = [&](int ph) __attribute__((always_inline)) {
     if (ph == ev_ph) {
       ev_ph += 2;
@@ -985,7 +984,7 @@ void fwd_pp_kernel(const FwdParams p) {
     // the previous item already. The query rows are read before the stream
     // may run on into the next item, whose rows take their place.
     issue_upto(min(c_t0 + STAGES, c_t0 + c_nt) - 1);
-    if (!ready) wait_for(c_t0);
+    if (idx == 0) wait_for(c_t0);         // later items: waited for at the previous item's end
     {
       int ln = lane;
       asm volatile("" : "+v"(ln));           // addresses made here, not kept from before the item loop
@@ -997,7 +996,11 @@ void fwd_pp_kernel(const FwdParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     issue_upto(c_t0 + STAGES - 1);
-    barrier();
+    // The first item's first tile is published here; a later item's was
+    // published by the barrier after the previous item's outputs. Without a
+    // barrier here group 0 goes on to its first unit while group 1 finishes
+    // this set-up (both groups still reach the same barriers).
+    if (idx == 0) barrier();
 
     wrow0 = c_w0;
     asm volatile("" : "+v"(wrow0));
@@ -1071,15 +1074,15 @@ void fwd_pp_kernel(const FwdParams p) {
       }
     }
     if (grp == 0) phase_begin(nph - 1);              // group 0 idles through the last phase
-    // The next item's first tile and query rows were issued at least two
-    // phases ago; they are waited for before this item's outputs are stored
-    // (stores count in vmcnt too: a wait after them would wait for them).
-    // Only the next item's second tile may be younger.
-    ready = false;
-    if (nx_nt > 0 && issued > c_t0 + c_nt) {
+    // The next item's first tile and query rows (issued at least two phases
+    // ago; its stage held a tile that every wave has finished with) are
+    // waited for before this item's outputs are stored: stores count in
+    // vmcnt too, so a wait after them would wait for them. Only the next
+    // item's second tile may be younger.
+    if (nx_nt > 0) {
+      issue_upto(c_t0 + c_nt);
       if (issued > c_t0 + c_nt + 1) wait_vmcnt<2 * LPW>();
       else wait_vmcnt<0>();
-      ready = true;
     }
 
     if (row < c_nq) {
@@ -1107,8 +1110,7 @@ void fwd_pp_kernel(const FwdParams p) {
       }
     }
     if (nx_nt == 0) break;                            // no next item
-    barrier();                                        // the last phase's reads end before its stage is refilled
-    issue_upto(c_t0 + c_nt);                          // the next item's first tile (normally issued already)
+    barrier();                                        // the last phase's reads end; the next item's first tile is published
     ++idx;
     c_t0 += c_nt;
     c_nt = nx.ntiles; c_nk = nx.nk; c_jb = nx.jbase; c_w0 = nx.w0; c_nq = nx.nq;
