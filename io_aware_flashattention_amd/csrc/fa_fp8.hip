@@ -21,9 +21,10 @@
 // moves with the row maximum (one FMA and one exponential per score; every
 // rescale is an exact power of two and every weight keeps three mantissa bits
 // down to 2^-14 of the largest). O is divided by the sum of the quantised
-// weights (one more MFMA, against an fp4 operand of ones) and multiplied by
-// V's scale; the LSE uses the float32 sum. Each wave issues the score MFMAs
-// of tile j+1 before the softmax of tile j, so the matrix cores run during
+// weights (one more, smaller MFMA against a lane-selected operand of ones)
+// and multiplied by V's scale; the LSE uses the float32 sum. Each wave
+// issues the score MFMAs of tile j+1 before the softmax of tile j, so the
+// matrix cores run during
 // the vector work; tiles arrive through a four-stage LDS ring.
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -334,14 +335,22 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
     const u32x4 c = row < n ? *reinterpret_cast<const u32x4*>(qp + 16) : u32x4{0, 0, 0, 0};
     qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
-  // 1.0 in every e2m1 (fp4) nibble: as the fp4 A operand of the weight-sum
-  // product it covers a lane's 32 k values in four registers
-  const i32x8 ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+  // Weight sums on v_mfma_scale_f32_16x16x128_f8f6f4. Read as its B operand,
+  // the P^T register of lane l (row l % 32, keys 32 (l / 32) ..) is column
+  // l % 16 of k-group l / 16: groups 0 and 2 hold rows 0-15, groups 1 and 3
+  // rows 16-31. The e4m3 A operand is 1.0 (0x38) where the parity of the
+  // k-group matches bit 2 of the A row m = l % 16, else 0: output row m then
+  // sums row (column) + 16 ((m / 4) & 1), so all four accumulator registers
+  // of lane l (rows 4 (l / 16) .. +3) hold its own row's sum. The sum of a
+  // tile's e4m3 weights (multiples of 2^-9 below 2^15) is exact in float32.
+  const int sel1 = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;
+  const i32x8 ones = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
 
   const float c2 = p.scale_log2 * qs;
   float m_run = kNegInf, l_run = 0.f;
   i32x8 pf = {};                             // this tile's e4m3 weights (B operand of O^T += V^T P^T)
-  f32x16 o[4], ls = f32x16{};                // ls: the last tile's sum of e4m3 weights, every register
+  f32x16 o[4];
+  f32x4 ls = f32x4{};                        // the last tile's sum of e4m3 weights, every register
   float l8 = 0.f;                            // sum of e4m3 weights of the earlier tiles
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
@@ -435,7 +444,7 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
       const i32x8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
       o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[db], 0, 0, 0, 127, 0, 127);
     }
-    ls = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, f32x16{}, 4, 0, 0, 127, 0, 127);   // A: fp4
+    ls = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, f32x4{}, 0, 0, 0, 127, 0, 127);
   };
 
   // Software pipeline: step j issues the score MFMAs of tile j+1, which run on
