@@ -90,6 +90,22 @@ def test_bwd_gqa_2k(causal):
         check_grad(a, b, f"{name} 2k causal={causal}")
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_bwd_kv_heads_grouped_per_xcd(d, causal):
+    """Batch x kv heads a multiple of 8 (here 2 x 4): each kv head's dK/dV
+    workgroups and dQ's query heads are dealt to one XCD, and dK/dV walks the
+    rows in the order that keeps them in step (down, then up). Ragged length,
+    more than one pass pair per workgroup; run twice, identical bits."""
+    say(f"case bwd B=2 Hq=16 Hkv=4 N=700 d={d} causal={causal} (kv heads grouped per XCD)")
+    got, ref, (qd, kd, vd, o, gd, lse, scale) = run_case(2, 16, 4, 700, d, causal, seed=990 + d)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(a, b, f"{name} grouped d={d} causal={causal}")
+    again = fa().bwd(qd, kd, vd, o, gd, lse, causal=causal, scale=scale, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(again, got):
+        assert torch.equal(a, b)
+
+
 def test_bwd_bf16_grads_are_rounded_fp32_grads():
     say("case bwd bf16 gradients == RNE(fp32 gradients)")
     got32, _, (qd, kd, vd, o, gd, lse, scale) = run_case(1, 4, 4, 200, 128, True, seed=960)
