@@ -193,7 +193,13 @@ void fwd_bf16_kernel(const FwdParams p) {
   if (L < 0) return;                         // padding of the last XCD round (whole workgroup)
   int g, t, kvh, b;
   if (CAUSAL && p.cu_seqlens == nullptr) {
-    L = blockIdx.x;
+    // Block b shares a compute unit with b + C, b + 2C, ... (C = the CU
+    // count) while they are all resident, so the heavy-first ranks snake
+    // across those slots: the CU that takes a heavy tile first takes a light
+    // one next, and every CU's blocks add up to about the same work.
+    const int C = p.cu_count, k = blockIdx.x / C, j = blockIdx.x - k * C;
+    const int cnt = min(C, (int)gridDim.x - k * C);
+    L = k * C + ((k & 1) ? cnt - 1 - j : j);
     const int nh = p.batch * p.heads_q;
     t = L / nh;
     L -= t * nh;
@@ -1127,18 +1133,6 @@ void fwd_pp_kernel(const FwdParams p) {
 
 namespace {
 
-template <int D, bool CAUSAL, typename TOut, int NW, int R, int STAGES>
-hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  constexpr int BRW = 32 * R * NW;
-  FwdParams q = p;
-  q.n_qtiles = (p.seqlen_q + BRW - 1) / BRW;
-  q.n_items = q.batch * q.heads_q * q.n_qtiles;
-  const int64_t wgs = grid_for(q);
-  hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, R, STAGES>), dim3((unsigned)wgs), dim3(NW * 64),
-                     0, stream, q);
-  return hipGetLastError();
-}
-
 // Compute units of the current device (the persistent grid's size), looked
 // up once per device. Concurrent first calls may both query the runtime; each
 // stores the same value, and the relaxed atomics make that race-free.
@@ -1152,6 +1146,19 @@ inline int device_cus() {
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+template <int D, bool CAUSAL, typename TOut, int NW, int R, int STAGES>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  constexpr int BRW = 32 * R * NW;
+  FwdParams q = p;
+  q.n_qtiles = (p.seqlen_q + BRW - 1) / BRW;
+  q.n_items = q.batch * q.heads_q * q.n_qtiles;
+  q.cu_count = device_cus();
+  const int64_t wgs = grid_for(q);
+  hipLaunchKernelGGL((detail::fwd_bf16_kernel<D, CAUSAL, TOut, NW, R, STAGES>), dim3((unsigned)wgs), dim3(NW * 64),
+                     0, stream, q);
+  return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, typename TOut, int STAGES>

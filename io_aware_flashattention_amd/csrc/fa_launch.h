@@ -36,6 +36,7 @@ struct FwdParams {
   // d = 128 kernel: an item is 256 >> hp_log2 query rows of 1 << hp_log2 query
   // heads that share a kv head (set by its launcher; 0 elsewhere)
   int hp_log2;
+  int cu_count;      // d = 64 kernel: compute units of the device (set by its launcher)
 };
 
 // The reciprocal (m, s) of d >= 1 described at FwdParams::div_m. With
