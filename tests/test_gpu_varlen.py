@@ -127,3 +127,19 @@ def test_varlen_mixed_lengths_gqa():
     # storage alone moves a value by up to 2^-7, so the oracle gate runs on the float32 output)
     o16, _ = _run(*dev, int(lens.max()), True, None, out_dtype=torch.bfloat16)
     assert torch.equal(o16, o.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 100)])
+def test_varlen_kv_heads_per_xcd(d, causal, window):
+    """Eight kv heads (a multiple of 8): each XCD takes one kv head of every
+    sequence, the sequences one after another. Lengths include an empty and
+    a one-token sequence, ragged tiles and a long tail."""
+    lens = [300, 0, 1, 129, 64, 777, 31]
+    say(f"case varlen kv heads per XCD d={d} lens={lens} causal={causal} window={window}")
+    q, k, v, cu = W.make_varlen_inputs(16, 8, d, lens, seed=800 + d)
+    dev = dict(q=to_dev(q), k=to_dev(k), v=to_dev(v), cu=torch.from_numpy(cu).to("cuda"))
+    o, lse = _run(dev["q"], dev["k"], dev["v"], dev["cu"], max(lens), causal, window)
+    o_ref, l_ref = varlen_ref(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, 1.0 / np.sqrt(d), causal=causal,
+                              window=window)
+    check(o, lse, o_ref, l_ref, f"varlen kv/XCD d={d} causal={causal} window={window}")
