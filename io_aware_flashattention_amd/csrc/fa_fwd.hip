@@ -1114,25 +1114,56 @@ void fwd_pp_kernel(const FwdParams p) {
       else wait_vmcnt<0>();
     }
 
-    if (row < c_nq) {
+    if constexpr (sizeof(TOut) == 2) {
+      // bf16 out: lanes l and l ^ 32 hold 4-column halves of the same 8
+      // columns of a row; one swap gives each lane 8 consecutive columns, so
+      // a row goes out in 16-byte stores
       const float l_o = lsum[0];
       const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
       TOut* op = reinterpret_cast<TOut*>(p.o) + c_o + (int64_t)row * p.o_stride[2];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int d = 32 * db + 8 * gq + 4 * half;
-          const float v0 = o[db][4 * gq + 0] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
-          const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
-          if constexpr (sizeof(TOut) == 4) {
-            *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
-          } else {
-            bf16x4 h;
-            h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
-            *reinterpret_cast<bf16x4*>(op + d) = h;
+        for (int m = 0; m < 2; ++m) {
+          uint32_t w[2][2];                    // [chunk 2m, 2m+1][dword]: 4 bf16 of this lane
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int gq = 2 * m + c;
+            bf16x2 a, bb;
+            a[0] = (__bf16)(o[db][4 * gq + 0] * inv_l); a[1] = (__bf16)(o[db][4 * gq + 1] * inv_l);
+            bb[0] = (__bf16)(o[db][4 * gq + 2] * inv_l); bb[1] = (__bf16)(o[db][4 * gq + 3] * inv_l);
+            w[c][0] = __builtin_bit_cast(uint32_t, a);
+            w[c][1] = __builtin_bit_cast(uint32_t, bb);
           }
+          // half 0 sends chunk 2m+1 and keeps 2m; half 1 sends 2m and keeps 2m+1
+          uint32_t got[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t send = half ? w[0][e] : w[1][e];
+            const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            got[e] = half ? r[0] : r[1];     // the partner lane's value
+          }
+          u32x4 out;
+          if (half == 0) out = u32x4{w[0][0], w[0][1], got[0], got[1]};
+          else out = u32x4{got[0], got[1], w[1][0], w[1][1]};
+          if (row < c_nq) *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m + 8 * half) = out;
         }
+    }
+    if (row < c_nq) {
+      if constexpr (sizeof(TOut) == 4) {
+        const float l_o = lsum[0];
+        const float inv_l = l_o > 0.f ? 1.f / l_o : 0.f;
+        TOut* op = reinterpret_cast<TOut*>(p.o) + c_o + (int64_t)row * p.o_stride[2];
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d = 32 * db + 8 * gq + 4 * half;
+            const float v0 = o[db][4 * gq + 0] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
+            const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
+            *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+          }
+      }
       if (p.lse != nullptr && half == 0) {
         const float lse = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
         p.lse[c_lse + row] = lse;
