@@ -481,24 +481,48 @@ void fwd_fp8_kernel(const Fp8FwdParams p) {
   }
   l8 += ls[0];
 
-  if (row < n) {
-    const float inv_l = l8 > 0.f ? vs / l8 : 0.f;
-    TOut* op = reinterpret_cast<TOut*>(p.o) + (((int64_t)b * p.heads_q + hq) * n + row) * D8;
+  const float inv_l = l8 > 0.f ? vs / l8 : 0.f;
+  TOut* op = reinterpret_cast<TOut*>(p.o) + (((int64_t)b * p.heads_q + hq) * n + row) * D8;
+  if constexpr (sizeof(TOut) == 2) {
+    // lanes l and l ^ 32 hold 4-column halves of the same 8 columns of a row:
+    // one swap per dword gives each lane 8 consecutive columns
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * half;
-        const float v0 = o[db][4 * gq] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
-        const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
-        if constexpr (sizeof(TOut) == 4) {
-          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
-        } else {
-          bf16x4 hh;
-          hh[0] = (__bf16)v0; hh[1] = (__bf16)v1; hh[2] = (__bf16)v2; hh[3] = (__bf16)v3;
-          *reinterpret_cast<bf16x4*>(op + d) = hh;
+      for (int m = 0; m < 2; ++m) {
+        uint32_t w[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int gq = 2 * m + c;
+          bf16x2 a, bb;
+          a[0] = (__bf16)(o[db][4 * gq] * inv_l); a[1] = (__bf16)(o[db][4 * gq + 1] * inv_l);
+          bb[0] = (__bf16)(o[db][4 * gq + 2] * inv_l); bb[1] = (__bf16)(o[db][4 * gq + 3] * inv_l);
+          w[c][0] = __builtin_bit_cast(uint32_t, a);
+          w[c][1] = __builtin_bit_cast(uint32_t, bb);
         }
+        uint32_t got[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t send = half ? w[0][e] : w[1][e];
+          const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+          got[e] = half ? r[0] : r[1];
+        }
+        const u32x4 out = half == 0 ? u32x4{w[0][0], w[0][1], got[0], got[1]} : u32x4{got[0], got[1], w[1][0], w[1][1]};
+        if (row < n) *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m + 8 * half) = out;
       }
+  }
+  if (row < n) {
+    if constexpr (sizeof(TOut) == 4) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * half;
+          const float v0 = o[db][4 * gq] * inv_l, v1 = o[db][4 * gq + 1] * inv_l;
+          const float v2 = o[db][4 * gq + 2] * inv_l, v3 = o[db][4 * gq + 3] * inv_l;
+          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+        }
+    }
     if (p.lse != nullptr && half == 0)
       p.lse[((int64_t)b * p.heads_q + hq) * n + row] = l_run > 0.f ? (m_run + __log2f(l_run) - 8.f) * kLn2 : kNegInf;
   }

@@ -505,24 +505,48 @@ void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
   for (int rb = 0; rb < R; ++rb) {
     const int row = wrow0 + 32 * rb + r32;
-    if (row >= nq) continue;
     const float inv_l = l_o[rb] > 0.f ? 1.f / l_o[rb] : 0.f;
     TOut* op = reinterpret_cast<TOut*>(p.o) + sv.o + (int64_t)row * p.o_stride[2];
+    if constexpr (sizeof(TOut) == 2) {
+      // lanes l and l ^ 32 hold 4-column halves of the same 8 columns of a
+      // row: one swap per dword gives each lane 8 consecutive columns
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+      for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * half;
-        const float v0 = o[rb][db][4 * gq + 0] * inv_l, v1 = o[rb][db][4 * gq + 1] * inv_l;
-        const float v2 = o[rb][db][4 * gq + 2] * inv_l, v3 = o[rb][db][4 * gq + 3] * inv_l;
-        if constexpr (sizeof(TOut) == 4) {
-          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
-        } else {
-          bf16x4 h;
-          h[0] = (__bf16)v0; h[1] = (__bf16)v1; h[2] = (__bf16)v2; h[3] = (__bf16)v3;
-          *reinterpret_cast<bf16x4*>(op + d) = h;
+        for (int m = 0; m < 2; ++m) {
+          uint32_t w[2][2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int gq = 2 * m + c;
+            bf16x2 a, bb;
+            a[0] = (__bf16)(o[rb][db][4 * gq + 0] * inv_l); a[1] = (__bf16)(o[rb][db][4 * gq + 1] * inv_l);
+            bb[0] = (__bf16)(o[rb][db][4 * gq + 2] * inv_l); bb[1] = (__bf16)(o[rb][db][4 * gq + 3] * inv_l);
+            w[c][0] = __builtin_bit_cast(uint32_t, a);
+            w[c][1] = __builtin_bit_cast(uint32_t, bb);
+          }
+          uint32_t got[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t send = half ? w[0][e] : w[1][e];
+            const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            got[e] = half ? r[0] : r[1];
+          }
+          const u32x4 out = half == 0 ? u32x4{w[0][0], w[0][1], got[0], got[1]} : u32x4{got[0], got[1], w[1][0], w[1][1]};
+          if (row < nq) *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m + 8 * half) = out;
         }
-      }
+    }
+    if (row >= nq) continue;
+    if constexpr (sizeof(TOut) == 4) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * half;
+          const float v0 = o[rb][db][4 * gq + 0] * inv_l, v1 = o[rb][db][4 * gq + 1] * inv_l;
+          const float v2 = o[rb][db][4 * gq + 2] * inv_l, v3 = o[rb][db][4 * gq + 3] * inv_l;
+          *reinterpret_cast<f32x4*>(op + d) = f32x4{v0, v1, v2, v3};
+        }
+    }
     if (p.lse != nullptr && half == 0) {
       const float lse = l_run[rb] > 0.f ? (m_run[rb] + __log2f(l_run[rb])) * kLn2 : kNegInf;
       p.lse[sv.lse + row] = lse;
