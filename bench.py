@@ -21,9 +21,13 @@ unmasked, and the 16384-token GQA prefill), each with its own algorithmic
 TFLOP/s, fraction of peak, HBM counter bytes when the committed counter
 summary matches the kernel sources, and the fp64 oracle timed on a bounded
 sample of the same configuration.
-Inputs are generated and uploaded before the timed region. W untimed warmup
-steps, then exactly K timed steps between two device synchronisations. Kernel
-durations come from HIP events recorded on the stream the kernels run on.
+Every phase's inputs are generated and uploaded before the first timed
+region, so the phases then run back to back: the shader clock drops while the
+GPU idles (as it does while the host generates inputs) and needs a few tens of
+milliseconds of load to come back up. Each phase runs W untimed warm-up
+launches (default 100: about 0.18 s of the step), then exactly K timed ones
+between two device synchronisations. Kernel durations come from HIP events
+recorded on the stream the kernels run on.
 
 Prints one JSON line. ``value`` is the prefill throughput in algorithmic
 TFLOP/s (4*B*Hq*N^2*d, halved for the causal mask); the decode bandwidth in
@@ -121,6 +125,27 @@ def run(args):
     cdst.copy_(csrc)
     torch.cuda.synchronize()
     del csrc, cdst
+    # the later phases' inputs, generated now so the timed phases run back to back
+    print(f"[bench] generating the paged form of {dc.name} (page size {PAGE_SIZE}, token-major)",
+          file=sys.stderr, flush=True)
+    _, pk, pv, ptab, plens = W.make_paged_decode_inputs(dc, PAGE_SIZE, layout="token", pad="zero")
+    assert np.array_equal(plens, lens)
+    pk_d, pv_d = to_dev(pk).transpose(1, 2), to_dev(pv).transpose(1, 2)   # indexed [page, kv head, slot, d]
+    del pk, pv
+    ptab_d = torch.from_numpy(ptab).to(dev)
+    varlen_in = {}
+    for name in ("c7_window_8k", "c6_varlen_causal"):
+        vc = W.VARLEN_CONFIGS[name]
+        vl = W.varlen_lengths(vc)
+        vq, vk, vv, vcu = W.make_varlen_inputs(vc.heads_q, vc.heads_kv, vc.head_dim, vl, seed=vc.seed)
+        varlen_in[name] = (vc, vl, to_dev(vq), to_dev(vk), to_dev(vv), torch.from_numpy(vcu).to(dev))
+        del vq, vk, vv
+    gh, _, _ = W.make_random_prefill(pc.batch, pc.heads_q, pc.heads_kv, pc.seqlen, pc.seqlen, pc.head_dim,
+                                     seed=pc.seed + 100)
+    dout = to_dev(gh)                        # dO of the backward
+    del gh
+    config_in = config_inputs(W, to_dev, dev)
+    torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
 
@@ -152,14 +177,6 @@ def run(args):
     print(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms wall", file=sys.stderr, flush=True)
 
     # paged-KV decode of the same workload, timed on its own after the steps
-    print(f"[bench] generating the paged form of {dc.name} (page size {PAGE_SIZE}, token-major)",
-          file=sys.stderr, flush=True)
-    _, pk, pv, ptab, plens = W.make_paged_decode_inputs(dc, PAGE_SIZE, layout="token", pad="zero")
-    assert np.array_equal(plens, lens)
-    pk_d, pv_d = to_dev(pk).transpose(1, 2), to_dev(pv).transpose(1, 2)   # indexed [page, kv head, slot, d]
-    del pk, pv
-    ptab_d = torch.from_numpy(ptab).to(dev)
-
     def paged():
         fa.decode_paged(dq_d, pk_d, pv_d, ptab_d, lens_d, scale=dc.scale, out=do, lse=dlse, workspace=ws)
 
@@ -190,11 +207,7 @@ def run(args):
     # packed prefill: sliding window and mixed lengths, each timed on its own
     extra = {}
     for key, name in (("prefill_window", "c7_window_8k"), ("prefill_varlen", "c6_varlen_causal")):
-        vc = W.VARLEN_CONFIGS[name]
-        vl = W.varlen_lengths(vc)
-        vq, vk, vv, vcu = W.make_varlen_inputs(vc.heads_q, vc.heads_kv, vc.head_dim, vl, seed=vc.seed)
-        vq, vk, vv = to_dev(vq), to_dev(vk), to_dev(vv)
-        vcu = torch.from_numpy(vcu).to(dev)
+        vc, vl, vq, vk, vv, vcu = varlen_in.pop(name)
         vo = torch.empty_like(vq)
         vlse = torch.empty(vc.heads_q, int(vl.sum()), dtype=torch.float32, device=dev)
         win = vc.window if vc.window >= 0 else None
@@ -227,9 +240,6 @@ def run(args):
                             "kernel": "fa_fwd_fp8 (fa_fp8_quantize timed apart)"}
     del quant, o8
     # backward of the step's prefill (same inputs, its O and LSE, a seeded dO)
-    gh, _, _ = W.make_random_prefill(pc.batch, pc.heads_q, pc.heads_kv, pc.seqlen, pc.seqlen, pc.head_dim,
-                                     seed=pc.seed + 100)
-    dout = to_dev(gh)
     fa.fwd(q, k, v, causal=True, scale=pc.scale, out=o, lse=lse)
     gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(fa.load().fa_bwd_workspace_bytes(pc.batch, pc.heads_q, pc.seqlen), dtype=torch.uint8,
@@ -243,7 +253,7 @@ def run(args):
                          "kernel": "fa_bwd (pre-pass + dK/dV + dQ)"}
     del dout, gq, gk, gv, bws
 
-    configs = config_phases(args, fa, W, cm, to_dev, time_launches, dev)
+    configs = config_phases(config_in, fa, W, cm, time_launches, dev)
     clock = None if args.no_clock else observed_clock(
         lambda: fa.fwd(q, k, v, causal=True, scale=pc.scale, out=o, lse=lse), sum(pre_ms) / len(pre_ms))
 
@@ -368,20 +378,31 @@ def observed_clock(launch, launch_ms: float, seconds: float = 2.5, settle: float
             pass
 
 
-def config_phases(args, fa, W, cm, to_dev, time_launches, dev):
-    """Every other prefill configuration, timed on its own with HIP events:
-    algorithmic TFLOP/s (4 B Hq N^2 d, halved for causal), fraction of the bf16
-    peak. The fp32 single head is launch-bound (its bar is parity)."""
+def config_inputs(W, to_dev, dev):
+    """Device inputs of every configuration in CONFIG_PHASES (generated before
+    the first timed region)."""
     import numpy as np
     import torch
     out = {}
     for name in CONFIG_PHASES:
         c = W.CONFIGS[name]
-        t0 = time.time()
         qh, kh, vh = W.make_prefill_inputs(c)
         up = (lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)) if c.dtype == "fp32" else to_dev
-        q, k, v = up(qh), up(kh), up(vh)
+        out[name] = (up(qh), up(kh), up(vh))
         del qh, kh, vh
+    return out
+
+
+def config_phases(config_in, fa, W, cm, time_launches, dev):
+    """Every other prefill configuration, timed on its own with HIP events:
+    algorithmic TFLOP/s (4 B Hq N^2 d, halved for causal), fraction of the bf16
+    peak. The fp32 single head is launch-bound (its bar is parity)."""
+    import torch
+    out = {}
+    for name in CONFIG_PHASES:
+        c = W.CONFIGS[name]
+        t0 = time.time()
+        q, k, v = config_in.pop(name)
         o = torch.empty(q.shape, dtype=torch.bfloat16 if c.dtype == "bf16" else torch.float32, device=dev)
         lse = torch.empty(c.batch, c.heads_q, c.seqlen, dtype=torch.float32, device=dev)
         ms = time_launches(lambda: fa.fwd(q, k, v, causal=c.causal, scale=c.scale, out=o, lse=lse))
@@ -393,7 +414,7 @@ def config_phases(args, fa, W, cm, to_dev, time_launches, dev):
                                  f"{'causal' if c.causal else 'no mask'}, {c.dtype} in, {o.dtype} out".replace(
                                      "torch.", ""),
                      "kernel": "fa_fwd"}
-        print(f"[bench] {name}: {ms:.4f} ms, {tf:.1f} TFLOP/s ({time.time() - t0:.1f}s with input generation)",
+        print(f"[bench] {name}: {ms:.4f} ms, {tf:.1f} TFLOP/s ({time.time() - t0:.2f}s)",
               file=sys.stderr, flush=True)
         del q, k, v, o, lse
     return out
@@ -726,7 +747,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock after the timed regions")
