@@ -45,7 +45,7 @@ def bench_dispatches(n):
     for _ in range(n):
         seq += BWD
     for cfg, kern in zip(bench.CONFIG_PHASES, (F32, FWD64, FWD, FWD_NONE, FWD)):
-        seq += [(kern, f"prefill {cfg}")] * n
+        seq += [(kern, f"prefill {cfg}")] * (n + bench.CONFIG_EXTRA_WARMUP.get(cfg, 0))
     return seq
 
 
