@@ -5,6 +5,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -28,15 +29,43 @@ PER_SOURCE = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-n
               "fa_bwd.hip": ["-fno-honor-nans"]}
 
 
+# Kernels whose waits count the vector-memory operations still in flight
+# (s_waitcnt vmcnt(N) with N > 0, so later tiles stay in flight). Scratch
+# spills are vector-memory operations too and would break those counts, so
+# the build refuses any of these kernels that uses scratch.
+COUNTED_WAITS = ("fwd_pp_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel")
+USAGE = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(remarks: str) -> list[str]:
+    """Kernels of COUNTED_WAITS that use scratch, from the compiler's
+    resource-usage remarks (a 'Function Name' line, then its 'ScratchSize')."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None:
+            if int(m.group(1)) > 0 and any(k in name for k in COUNTED_WAITS):
+                bad.append(name)
+            name = None
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     extra = PER_SOURCE.get(src, [])
-    cmd = [HIPCC, *COMMON, *extra, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *extra, *DEVICE, USAGE, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, "-x", "hip", *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    bad = scratch_users(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels with counted vmcnt waits use scratch (register spills): {bad}")
     return obj
 
 

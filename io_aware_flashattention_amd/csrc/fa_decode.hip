@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int kk = acc_key(jj, half);
-        sc[jj] = (kk >= valid) | (kk < lo) ? kNegInf : sc[jj];
+        sc[jj] = ((kk >= valid) | (kk < lo)) ? kNegInf : sc[jj];
       }
     }
     float mx = sc[0];
