@@ -1,5 +1,7 @@
 """Long contexts against the fp64 oracle: a 131,072-token causal GQA prefill
-on sampled rows, and decode over caches of up to 131,072 tokens in full.
+and a packed batch holding a 131,072-token sequence under a 4,096-token
+window, on sampled rows, and decode over caches of up to 131,072 tokens in
+full.
 Offsets, tile counters and the decode's token ranges all grow with the
 length, so these are the sizes where an index kept in too narrow a type
 would show."""
@@ -9,7 +11,7 @@ import torch
 
 import io_aware_flashattention_amd as fa
 from io_aware_flashattention_amd import workloads as W
-from oracle import attention_ref
+from oracle import attention_ref, varlen_ref
 from tests.parity import check, say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -51,3 +53,21 @@ def test_decode_128k_caches():
         ro, rl = attention_ref(W.to_f64(q[b])[None, :, None, :], W.to_f64(kc[b:b + 1, :, :n]),
                                W.to_f64(vc[b:b + 1, :, :n]), cfg.scale)
         check(o[b], l[b], ro[0, :, 0], rl[0, :, 0], f"decode b={b} L={n}")
+
+
+def test_packed_128k_window_sampled_rows():
+    lens = np.array([3000, N, 1], dtype=np.int64)
+    W_ = 4096
+    say(f"case packed lengths {lens.tolist()} Hq8 Hkv1 d128 causal window {W_}")
+    q, k, v, cu = W.make_varlen_inputs(8, 1, 128, lens, seed=23)
+    o, lse = fa.fwd_varlen(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(cu).to("cuda"), int(lens.max()),
+                           causal=True, window=W_, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s0 = int(cu[1])
+    rng = np.random.default_rng(23)
+    local = {0, 1, W_ - 1, W_, W_ + 1, W_ + 63, W_ + 64, N // 2, N - 65, N - 64, N - 1}
+    local |= set(rng.integers(0, N, 24).tolist())
+    rows = [0, 1, 2999] + [s0 + r for r in sorted(local)] + [int(cu[2])]
+    o_ref, l_ref = varlen_ref(q, k, v, cu, 1 / np.sqrt(128), causal=True, window=W_, rows=rows, values=W.to_f64)
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    check(o[rows], lse[:, rows], o_ref[rows], l_ref[:, rows], f"packed N{N} window {W_} [{len(rows)} sampled rows]")
