@@ -1,7 +1,7 @@
 """Long contexts against the fp64 oracle: a 131,072-token causal GQA prefill
 and a packed batch holding a 131,072-token sequence under a 4,096-token
 window, on sampled rows, and decode over caches of up to 131,072 tokens in
-full.
+full, contiguous and paged (the paged form bit for bit the contiguous one).
 Offsets, tile counters and the decode's token ranges all grow with the
 length, so these are the sizes where an index kept in too narrow a type
 would show."""
@@ -71,3 +71,19 @@ def test_packed_128k_window_sampled_rows():
     o_ref, l_ref = varlen_ref(q, k, v, cu, 1 / np.sqrt(128), causal=True, window=W_, rows=rows, values=W.to_f64)
     o, lse = o.cpu().numpy(), lse.cpu().numpy()
     check(o[rows], lse[:, rows], o_ref[rows], l_ref[:, rows], f"packed N{N} window {W_} [{len(rows)} sampled rows]")
+
+
+def test_paged_decode_128k_equals_contiguous():
+    lens = np.array([N, 5, 70001], dtype=np.int32)
+    cfg = W.DecodeConfig("long", 3, 16, 2, 1, N, 128, 22)
+    say(f"case paged decode B3 Hq16 Hkv2 lengths {lens.tolist()}, 16-token token-major pages")
+    q, kc, vc, _ = W.make_decode_inputs(cfg, pad="nan", lengths=lens)
+    dev_lens = torch.from_numpy(lens).to("cuda")
+    o_c, l_c = fa.decode(to_dev(q), to_dev(kc), to_dev(vc), dev_lens, scale=cfg.scale, out_dtype=torch.float32)
+    del kc, vc
+    q2, kp, vp, table, _ = W.make_paged_decode_inputs(cfg, 16, layout="token", pad="nan", lengths=lens)
+    assert np.array_equal(q2, q)
+    o_p, l_p = fa.decode_paged(to_dev(q), to_dev(kp).transpose(1, 2), to_dev(vp).transpose(1, 2),
+                               torch.from_numpy(table).to("cuda"), dev_lens, scale=cfg.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_c) and torch.equal(l_p, l_c)
