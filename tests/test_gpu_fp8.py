@@ -136,3 +136,29 @@ def test_fp8_long_context_gqa_sampled():
     so, sl = fp8_gate.error_model(q64, k64, v64, signs, cfg.scale, True, rows=rows)
     fp8_gate.gate(o_h, l_h, o_ex, l_ex, so, sl, f"fp8 {cfg.name} [{len(rows)} rows]", say=say)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_fp8_long_ragged_context_sampled():
+    """65,499 tokens (a ragged last tile and scale block), 8 query heads over
+    one kv head, causal, 1% of K rows x8: sampled rows against the FP8 oracle
+    and against exact attention through the e4m3 error model."""
+    N = 65499
+    say(f"case fp8 long context N={N} sampled rows")
+    q, k, v = W.make_random_prefill(1, 8, 1, N, N, 128, seed=1300, heavy_frac=0.01)
+    signs = signs_for(1300)
+    got = gpu_quant(q, k, v, signs)
+    o, lse = fa().fwd_fp8(got, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = {0, 1, 127, 128, 32767, 32768, N - 130, N - 129, N - 128, N - 64, N - 2, N - 1}
+    rows |= set(np.random.default_rng(1300).integers(0, N, 12).tolist())
+    rows = sorted(rows)
+    q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    quant = quantize(q64, k64, v64, signs)
+    scale = 1 / np.sqrt(128)
+    o_ref, l_ref = fp8_attention_ref(quant, scale, causal=True, rows=rows)
+    o_h, l_h = o[:, :, rows].cpu().numpy(), lse[:, :, rows].cpu().numpy()
+    _check(o[:, :, rows], lse[:, :, rows], o_ref[:, :, rows], l_ref[:, :, rows], f"fp8 N={N} [{len(rows)} rows]")
+    o_ex, l_ex = attention_ref(q64[:, :, rows], k64, v64, scale, causal=True, q_positions=np.array(rows))
+    so, sl = fp8_gate.error_model(q64, k64, v64, signs, scale, True, rows=rows)
+    fp8_gate.gate(o_h, l_h, o_ex, l_ex, so, sl, f"fp8 N={N} [{len(rows)} rows]", say=say)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
