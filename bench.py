@@ -26,8 +26,10 @@ region, so the phases then run back to back: the shader clock drops while the
 GPU idles (as it does while the host generates inputs) and needs a few tens of
 milliseconds of load to come back up. Each phase runs W untimed warm-up
 launches (default 100: about 0.18 s of the step), then exactly K timed ones
-between two device synchronisations. Kernel durations come from HIP events
-recorded on the stream the kernels run on.
+between two device synchronisations. Times come from HIP events recorded on
+the stream the kernels run on: around each kernel of the step and of the
+paged decode, and around the K back-to-back launches of every later phase
+(per launch: the span / K).
 
 Prints one JSON line. ``value`` is the prefill throughput in algorithmic
 TFLOP/s (4*B*Hq*N^2*d, halved for the causal mask); the decode bandwidth in
@@ -198,16 +200,19 @@ def run(args):
     del pk_d, pv_d
 
     def time_launches(fn, extra_warmup=0):
+        """ms per launch: K launches back to back between two HIP events, after
+        the warm-up (a pair of events around every launch would add the
+        events' own cost, ~3 us, to each of the short ones)."""
         for _ in range(args.warmup + extra_warmup):
             fn()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        for e in evs:
-            e[0].record(stream)
+        e0.record(stream)
+        for _ in range(args.steps):
             fn()
-            e[1].record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+        return e0.elapsed_time(e1) / args.steps
 
     # packed prefill: sliding window and mixed lengths, each timed on its own
     extra = {}
